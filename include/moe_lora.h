@@ -1,0 +1,190 @@
+/*
+ * moe_lora.h — C ABI of the MI355X (gfx950) routed MoE-LoRA expert layer.
+ *
+ * The layer (one MoE block with per-expert LoRA adapters) is split into the four
+ * stages the pages' bf16 pipeline names — routing -> permute -> gate_up GEMM,
+ * activation, down GEMM -> finalize (sglang PR "[LoRA] bf16 MoE-LoRA for trtllm
+ * backend with two-stream overlap + routing opts", Files-changed table, launcher
+ * row; section 1(A) single-stream flow) — as four calls:
+ *
+ *   moe_lora_route     top-k routing + expert-sorted pack, one launch
+ *   moe_lora_permute   gather token rows into expert-sorted order
+ *   moe_lora_forward   gate_up GEMM + LoRA delta (before SwiGLU) + SwiGLU
+ *                      + down GEMM + down LoRA delta, unweighted, permuted rows
+ *   moe_lora_finalize  routing-weighted top-k reduction back to token order
+ *
+ * Conventions (all calls):
+ *   - Tensor pointers are DEVICE pointers unless marked [host].  bf16 tensors are
+ *     passed as uint16_t bit patterns.  Every device pointer must be 16-byte aligned.
+ *   - All layouts are row-major with the last dimension contiguous.
+ *   - The caller owns every buffer, including the workspaces sized by the
+ *     *_workspace_size functions; the library never allocates device memory
+ *     (the capture-safety lesson of sglang PR "[LoRA] Fix experimental fast-path
+ *     multi-adapter correctness ...", Motivation item 3 and Modifications).
+ *   - Work is enqueued on the given stream(s) (a hipStream_t passed as void*;
+ *     NULL = the null stream) and is asynchronous.  No call synchronizes the device.
+ *   - Errors: arguments are validated on the host first; on any error nothing is
+ *     enqueued and a nonzero moe_lora_status is returned.  A launch failure returns
+ *     MOE_LORA_ERR_HIP.  Device-side faults surface at the caller's next
+ *     synchronization.  num_tokens == 0 is a valid no-op.
+ *   - Row indices: the expanded index of (token t, choice j) is t*top_k + j (vLLM API
+ *     page "trtllm_lora_moe", _unpermute_activation).  "Permuted" rows are ordered by
+ *     expert, and inside one expert by ascending expanded index.
+ */
+#ifndef MOE_LORA_H
+#define MOE_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *moe_lora_stream_t; /* hipStream_t */
+
+typedef enum {
+  MOE_LORA_OK = 0,
+  MOE_LORA_ERR_INVALID_ARGUMENT = 1,
+  MOE_LORA_ERR_UNSUPPORTED = 2,
+  MOE_LORA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_LORA_ERR_HIP = 4
+} moe_lora_status;
+
+/* Routing methods (vLLM API page "trtllm_lora_moe", TrtLlmBf16LoRAExperts
+ * ._supports_routing_method).  RenormalizeNaive computes the same ids and weights
+ * as Renormalize (softmax is monotone), so it shares the enum value. */
+typedef enum {
+  MOE_LORA_ROUTING_RENORMALIZE = 0,
+  MOE_LORA_ROUTING_DEEPSEEK_V3 = 1
+} moe_lora_routing;
+
+#define MOE_LORA_MAX_SLOTS 8
+#define MOE_LORA_MAX_RANK 64   /* direct-expand limit, section 2 of the bf16 PR */
+#define MOE_LORA_MAX_EXPERTS 512
+#define MOE_LORA_MAX_TOPK 32
+
+/* Problem size (the (E, M, N=2I, K=H, topk) tuple of the vLLM API page,
+ * _TrtLlmLoRAExpertsBase.moe_problem_size). */
+typedef struct {
+  int32_t num_tokens;  /* T >= 0 */
+  int32_t hidden;      /* H, multiple of 8 */
+  int32_t inter;       /* I, multiple of 8 (expert intermediate size) */
+  int32_t num_experts; /* E in [1, MOE_LORA_MAX_EXPERTS] */
+  int32_t top_k;       /* k in [1, min(E, MOE_LORA_MAX_TOPK)] */
+} moe_lora_dims;
+
+/* DeepSeek-V3 grouped routing parameters (the n_group / topk_group /
+ * routed_scaling_factor arguments of the routed op on the vLLM API page). */
+typedef struct {
+  int32_t n_group;              /* E % n_group == 0, n_group <= 64 */
+  int32_t topk_group;           /* 1 <= topk_group <= n_group */
+  float routed_scaling_factor;  /* folded into the returned weights */
+  const float *correction_bias; /* [E] fp32, selection only; NULL = zeros */
+} moe_lora_grouped;
+
+/* Resident LoRA adapter slots.  A token's slot comes from token_slot[t]; a value
+ * outside [0, num_slots) means "no adapter" for that token (the -1 sentinel of the
+ * bf16 PR, section 2).  Slot, rank and scaling are looked up per token (sglang PR
+ * "[LoRA] Fix experimental fast-path multi-adapter correctness ...", Motivation
+ * item 2).  Weights are stored per slot, compactly (no padding to the largest rank):
+ *   a_gate_up[s]: [E, rank[s], H]     b_gate_up[s]: [E, 2I, rank[s]]  (rows: gate then up)
+ *   a_down[s]:    [E, rank[s], I]     b_down[s]:    [E, H, rank[s]]
+ * The gate_up delta s*B1(A1 x) is added before SwiGLU and is not routing-weighted;
+ * the down delta s*B2(A2 h) is added to the expert output (so finalize weights it). */
+typedef struct {
+  int32_t num_slots;           /* 0..MOE_LORA_MAX_SLOTS; 0 = base MoE */
+  const int32_t *token_slot;   /* [T] */
+  int32_t rank[MOE_LORA_MAX_SLOTS];   /* 1..MOE_LORA_MAX_RANK */
+  float scaling[MOE_LORA_MAX_SLOTS];
+  const uint16_t *a_gate_up[MOE_LORA_MAX_SLOTS];
+  const uint16_t *b_gate_up[MOE_LORA_MAX_SLOTS];
+  const uint16_t *a_down[MOE_LORA_MAX_SLOTS];
+  const uint16_t *b_down[MOE_LORA_MAX_SLOTS];
+} moe_lora_adapters;
+
+/* Optional knobs of moe_lora_forward (NULL = defaults). */
+typedef struct {
+  int32_t two_stream_max_tokens; /* side stream used only when T <= this (default 256) */
+  int32_t force_path;            /* 0 auto, 1 fused epilogues, 2 decomposed (delta + activation kernels) */
+  /* Optional hipEvent_t handles (NULL = none) recorded on `main` immediately before and
+   * after the gate_up GEMM launch, so a caller can time that kernel alone. */
+  void *gate_up_event_begin;
+  void *gate_up_event_end;
+  int32_t reserved[4];
+} moe_lora_options;
+
+/* Human-readable name of a status code (static storage). */
+const char *moe_lora_status_string(int status);
+
+/* Library ABI version (incremented on any signature change). */
+int moe_lora_version(void);
+
+/* ---------------------------------------------------------------- route
+ * Top-k routing and the expert-sorted pack in one launch (sglang PR "[LoRA]
+ * Experimental fast LoRA path ...", Optimizations: top-k and the routed pack in a
+ * single launch).
+ *   Renormalize: top-k of the bf16 logits (ties -> lower expert index), weights =
+ *     softmax over the k selected logits.
+ *   DeepSeek-V3: s = sigmoid(logit), key = s + correction_bias; groups are contiguous
+ *     blocks of E/n_group experts scored by the sum of their two largest keys; the
+ *     best topk_group groups (ties -> lower group index) are kept; the top-k keys in
+ *     them are chosen (ties -> lower index); weights = rsf * s / sum(s).
+ * Outputs:
+ *   topk_ids [T, k] int32 (descending key), topk_weights [T, k] fp32,
+ *   expert_offsets [E+1] int32 (exclusive prefix of per-expert counts),
+ *   expanded_to_permuted [T*k] int32, permuted_to_expanded [T*k] int32.
+ * Workspace: moe_lora_route_workspace_size(dims) bytes (may be 0 -> ws may be NULL).
+ * grouped must be non-NULL for MOE_LORA_ROUTING_DEEPSEEK_V3 and is ignored otherwise. */
+size_t moe_lora_route_workspace_size(const moe_lora_dims *dims);
+int moe_lora_route(const moe_lora_dims *dims, int routing, const moe_lora_grouped *grouped,
+                   const uint16_t *logits, int32_t *topk_ids, float *topk_weights,
+                   int32_t *expert_offsets, int32_t *expanded_to_permuted,
+                   int32_t *permuted_to_expanded, void *ws, size_t ws_bytes,
+                   moe_lora_stream_t stream);
+
+/* ---------------------------------------------------------------- permute
+ * x_perm[p, :] = x[permuted_to_expanded[p] / top_k, :]  (bf16 gather; the bf16 PR's
+ * "permute bf16 hidden" step).  x [T, H], x_perm [T*k, H]. */
+int moe_lora_permute(const moe_lora_dims *dims, const uint16_t *x,
+                     const int32_t *permuted_to_expanded, uint16_t *x_perm,
+                     moe_lora_stream_t stream);
+
+/* ---------------------------------------------------------------- forward
+ * For every permuted row p (token t = permuted_to_expanded[p] / top_k, expert e,
+ * slot a = token_slot[t]):
+ *   g = W1[e] x_t + [a valid] s_a B1[a][e] (A1[a][e] x_t)        (2I)
+ *   h = silu(g[0:I]) * g[I:2I]                                   (I)
+ *   y_perm[p] = W2[e] h + [a valid] s_a B2[a][e] (A2[a][e] h)    (H), unweighted
+ * (bf16 PR: Files-changed launcher row and section 2(A) steps 1-4; vLLM API page,
+ * _TrtLlmLoRAExpertsBase.apply.)  fp32 accumulation; bf16 output.
+ *   x       [T, H] token-order rows, or NULL when x_perm is given
+ *   x_perm  [T*k, H] permuted rows, or NULL: then rows are gathered from x on load
+ *   w_gate_up [E, 2I, H] (rows [0,I) gate, [I,2I) up), w_down [E, H, I]
+ *   lora    NULL or num_slots == 0 -> the base MoE (same kernels, no LoRA work)
+ *   y_perm  [T*k, H] output
+ *   side    optional second stream: the gate_up LoRA runs there, overlapped with the
+ *           base gate_up GEMM, and main waits on it before the activation; on return
+ *           all work is ordered before later work on `main`.  NULL = one stream.
+ *   opts    NULL = defaults.
+ * Workspace: moe_lora_forward_workspace_size(dims, lora) bytes. */
+size_t moe_lora_forward_workspace_size(const moe_lora_dims *dims, const moe_lora_adapters *lora);
+int moe_lora_forward(const moe_lora_dims *dims, const uint16_t *x, const uint16_t *x_perm,
+                     const int32_t *expert_offsets, const int32_t *permuted_to_expanded,
+                     const uint16_t *w_gate_up, const uint16_t *w_down,
+                     const moe_lora_adapters *lora, uint16_t *y_perm, void *ws, size_t ws_bytes,
+                     moe_lora_stream_t main, moe_lora_stream_t side,
+                     const moe_lora_options *opts);
+
+/* ---------------------------------------------------------------- finalize
+ * out[t, :] = bf16( sum_j topk_weights[t, j] * y_perm[expanded_to_permuted[t*k+j], :] ),
+ * summed in fp32 in j order (vLLM API page, _finalize_with_w2_lora).  out [T, H]. */
+int moe_lora_finalize(const moe_lora_dims *dims, const uint16_t *y_perm,
+                      const float *topk_weights, const int32_t *expanded_to_permuted,
+                      uint16_t *out, moe_lora_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LORA_H */

@@ -1,0 +1,135 @@
+"""The C-ABI library: it loads, exports every declared symbol, and its host-side
+validation rejects bad arguments before touching a device (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_02_amd as pkg
+from mixture_experts_ffn_02_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_lora.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_lora_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkg.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.moe_lora_version() == 1
+
+
+def test_status_strings():
+    assert _lib.status_string(0) == "ok"
+    assert "workspace" in _lib.status_string(3)
+    assert _lib.status_string(99) == "unknown status"
+
+
+def _dims(T=16, H=256, I=128, E=8, k=2):
+    return _lib.Dims(T, H, I, E, k)
+
+
+def test_workspace_sizes_are_host_only_and_grow_with_lora():
+    lib = pkg.load()
+    d = _dims()
+    assert lib.moe_lora_route_workspace_size(ctypes.byref(d)) == 1 * 8 * 4
+    base = lib.moe_lora_forward_workspace_size(ctypes.byref(d), None)
+    assert base >= 32 * 128 * 2
+    a = _lib.Adapters()
+    a.num_slots = 1
+    a.rank[0] = 16
+    with_lora = lib.moe_lora_forward_workspace_size(ctypes.byref(d), ctypes.byref(a))
+    assert with_lora > base
+    a.rank[0] = 65
+    assert lib.moe_lora_forward_workspace_size(ctypes.byref(d), ctypes.byref(a)) == 0
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("dims,status", [
+    ((16, 256, 128, 8, 0), _lib.ERR_INVALID_ARGUMENT),    # top_k = 0
+    ((16, 256, 128, 8, 9), _lib.ERR_INVALID_ARGUMENT),    # top_k > E
+    ((16, 256, 128, 513, 2), _lib.ERR_INVALID_ARGUMENT),  # too many experts
+    ((-1, 256, 128, 8, 2), _lib.ERR_INVALID_ARGUMENT),    # negative T
+    ((16, 252, 128, 8, 2), _lib.ERR_UNSUPPORTED),         # H not a multiple of 8
+    ((16, 256, 100, 8, 2), _lib.ERR_UNSUPPORTED),         # I not a multiple of 8
+])
+def test_bad_dims_rejected_before_launch(dims, status):
+    lib = pkg.load()
+    d = _lib.Dims(*dims)
+    r = lib.moe_lora_route(ctypes.byref(d), 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                           None)
+    assert r == status
+    assert lib.moe_lora_permute(ctypes.byref(d), FAKE, FAKE, FAKE, None) == status
+    assert lib.moe_lora_finalize(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+def test_route_argument_checks():
+    lib = pkg.load()
+    d = _dims(E=8)
+    g = _lib.Grouped(3, 1, 1.0, None)  # 8 % 3 != 0
+    assert lib.moe_lora_route(ctypes.byref(d), 1, ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, 1 << 20, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.moe_lora_route(ctypes.byref(d), 1, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              1 << 20, None) == _lib.ERR_INVALID_ARGUMENT
+    g = _lib.Grouped(4, 1, 1.0, None)  # top_k 2 fits one group of 2 experts
+    # workspace too small is reported before launch
+    assert lib.moe_lora_route(ctypes.byref(d), 1, ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, 0, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    g = _lib.Grouped(4, 1, 1.0, None)
+    d3 = _dims(k=3)  # 3 > topk_group * E / n_group = 2
+    assert lib.moe_lora_route(ctypes.byref(d3), 1, ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, 1 << 20, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.moe_lora_route(ctypes.byref(d), 7, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              1 << 20, None) == _lib.ERR_INVALID_ARGUMENT
+    # misaligned pointer
+    assert lib.moe_lora_route(ctypes.byref(d), 0, None, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              1 << 20, None) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_forward_argument_checks():
+    lib = pkg.load()
+    d = _dims()
+    a = _lib.Adapters()
+    a.num_slots = 9
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
+                                None, None) == _lib.ERR_INVALID_ARGUMENT
+    a.num_slots = 1
+    a.token_slot = FAKE
+    a.rank[0] = 80
+    for f in ("a_gate_up", "b_gate_up", "a_down", "b_down"):
+        getattr(a, f)[0] = FAKE
+    assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
+                                None, None) == _lib.ERR_UNSUPPORTED
+    a.rank[0] = 16
+    assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 16, None, None,
+                                None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    # neither x nor x_perm
+    assert lib.moe_lora_forward(ctypes.byref(d), None, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                1 << 30, None, None, None) == _lib.ERR_INVALID_ARGUMENT
+    a.b_down[0] = None
+    assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
+                                None, None) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_empty_batch_is_a_noop_without_device_work():
+    lib = pkg.load()
+    d = _dims(T=0)
+    assert lib.moe_lora_permute(ctypes.byref(d), None, None, None, None) == _lib.OK
+    assert lib.moe_lora_finalize(ctypes.byref(d), None, None, None, None, None) == _lib.OK
+    assert lib.moe_lora_forward(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
+                                0, None, None, None) == _lib.OK

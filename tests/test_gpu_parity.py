@@ -1,0 +1,262 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Integer outputs (top-k ids, expert offsets, both permutation maps) must match bit for
+bit; routing weights within 1e-5 relative; layer outputs within relative L2 1e-2 and
+max-abs 3e-2 (bf16 I/O with fp32 accumulation).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import GpuLayer, assert_layer_close, bits, dev, f64, say, t16
+from mixture_experts_ffn_02_amd import moe_lora as ml
+from synth import NAMED_CONFIGS, Workload, f32_to_bf16_bits, make_config
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = make_config(name="ragged_T37_H200_I88_E6_k3", cfg_id=201, T=37, H=200, I=88, E=6, top_k=3,
+                     slots=((3, 2.0), (8, 0.5), (13, 1.0)), slot_assignment="uniform",
+                     w_std=0.05, lora_a_std=0.1, lora_b_std=0.1)
+
+_CACHE = {}
+
+
+def gpu_layer(cfg, seed=0, stream_weights=False) -> GpuLayer:
+    key = (cfg, seed)
+    if key not in _CACHE:
+        say(f"[setup] {cfg.name} seed={seed}")
+        _CACHE.clear()  # keep at most one large workload resident
+        torch.cuda.empty_cache()
+        _CACHE[key] = GpuLayer(Workload(cfg, seed), stream_weights)
+    return _CACHE[key]
+
+
+def run_route(g: GpuLayer, T=None):
+    c = g.cfg
+    T = c.T if T is None else T
+    layer = g.layer()
+    d = layer.dims(T)
+    R = T * c.top_k
+    out = dict(ids=torch.empty((T, c.top_k), dtype=torch.int32, device=dev()),
+               w=torch.empty((T, c.top_k), dtype=torch.float32, device=dev()),
+               off=torch.empty((c.E + 1,), dtype=torch.int32, device=dev()),
+               e2p=torch.empty((R,), dtype=torch.int32, device=dev()),
+               p2e=torch.empty((R,), dtype=torch.int32, device=dev()))
+    ws = torch.empty((max(1, ml.moe_lora_route_workspace_size(d)),), dtype=torch.uint8, device=dev())
+    ml.moe_lora_route(d, g.logits[:T], out["ids"], out["w"], out["off"], out["e2p"], out["p2e"], ws,
+                      g.routing, layer.grouped)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def check_route(got, ids_ref, w_ref, E):
+    srt = oracle.expert_sort(ids_ref, E)
+    np.testing.assert_array_equal(got["ids"], ids_ref)
+    np.testing.assert_array_equal(got["off"], srt["offsets"])
+    np.testing.assert_array_equal(got["e2p"], srt["e2p"])
+    np.testing.assert_array_equal(got["p2e"], srt["p2e"])
+    np.testing.assert_allclose(got["w"], w_ref, rtol=1e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
+def test_route_parity_named_configs(cfg_id):
+    cfg = NAMED_CONFIGS[cfg_id]
+    wl = Workload(cfg)
+    say(f"[route] {cfg.name}")
+    logits, bias = wl.logits(), wl.correction_bias()
+    ids, w = oracle.route(logits, cfg.top_k, cfg.routing, bias, cfg.n_group, cfg.topk_group,
+                          cfg.routed_scaling_factor)
+    d = ml.dims(cfg.T, cfg.H, cfg.I, cfg.E, cfg.top_k)
+    R = cfg.R
+    o = dict(ids=torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev()),
+             w=torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev()),
+             off=torch.empty((cfg.E + 1,), dtype=torch.int32, device=dev()),
+             e2p=torch.empty((R,), dtype=torch.int32, device=dev()),
+             p2e=torch.empty((R,), dtype=torch.int32, device=dev()))
+    ws = torch.empty((ml.moe_lora_route_workspace_size(d),), dtype=torch.uint8, device=dev())
+    grouped = None
+    routing = ml.ROUTING_RENORMALIZE
+    bias_t = None
+    if cfg.routing == "deepseek_v3":
+        routing = ml.ROUTING_DEEPSEEK_V3
+        bias_t = torch.from_numpy(bias).to(dev())
+        grouped = ml.Grouped(cfg.n_group, cfg.topk_group, cfg.routed_scaling_factor, bias_t.data_ptr())
+    ml.moe_lora_route(d, t16(logits), o["ids"], o["w"], o["off"], o["e2p"], o["p2e"], ws, routing,
+                      grouped)
+    torch.cuda.synchronize()
+    check_route({k: v.cpu().numpy() for k, v in o.items()}, ids, w, cfg.E)
+
+
+def _route_case(T, E, k, logits_f32, routing="renormalize", bias=None, n_group=1, topk_group=1,
+                rsf=1.0):
+    lb = f32_to_bf16_bits(logits_f32)
+    ids, w = oracle.route(lb, k, routing, bias, n_group, topk_group, rsf)
+    d = ml.dims(T, 64, 64, E, k)
+    R = T * k
+    o = dict(ids=torch.empty((T, k), dtype=torch.int32, device=dev()),
+             w=torch.empty((T, k), dtype=torch.float32, device=dev()),
+             off=torch.empty((E + 1,), dtype=torch.int32, device=dev()),
+             e2p=torch.empty((R,), dtype=torch.int32, device=dev()),
+             p2e=torch.empty((R,), dtype=torch.int32, device=dev()))
+    ws = torch.empty((ml.moe_lora_route_workspace_size(d),), dtype=torch.uint8, device=dev())
+    grouped, r = None, ml.ROUTING_RENORMALIZE
+    if routing == "deepseek_v3":
+        r = ml.ROUTING_DEEPSEEK_V3
+        bt = torch.from_numpy(np.asarray(bias, np.float32)).to(dev())
+        grouped = ml.Grouped(n_group, topk_group, rsf, bt.data_ptr())
+    ml.moe_lora_route(d, t16(lb), o["ids"], o["w"], o["off"], o["e2p"], o["p2e"], ws, r, grouped)
+    torch.cuda.synchronize()
+    check_route({kk: v.cpu().numpy() for kk, v in o.items()}, ids, w, E)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (5, 6, 3), (63, 64, 8), (65, 65, 7), (300, 128, 8),
+                                   (129, 300, 32), (4097, 512, 4), (2000, 8, 2)])
+def test_route_shapes_with_heavy_ties(T, E, k):
+    say(f"[route ties] T={T} E={E} k={k}")
+    rng = np.random.default_rng(T * 7919 + E)
+    # values on a coarse grid: many exact ties, including +0 / -0
+    lg = (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)
+    lg[:, ::5] = -0.0
+    _route_case(T, E, k, lg)
+
+
+@pytest.mark.parametrize("T,E,k,ng,tg", [(33, 16, 4, 4, 2), (257, 256, 8, 8, 4), (70, 64, 6, 64, 6),
+                                         (10, 32, 2, 1, 1)])
+def test_route_deepseek_v3_shapes(T, E, k, ng, tg):
+    say(f"[route dsv3] T={T} E={E} k={k} groups={ng}/{tg}")
+    rng = np.random.default_rng(T + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    _route_case(T, E, k, lg, "deepseek_v3", bias, ng, tg, 2.5)
+
+
+def test_route_deepseek_v3_exact_ties():
+    say("[route dsv3 ties]")
+    rng = np.random.default_rng(77)
+    lg = (np.round(rng.standard_normal((50, 64)) * 2) / 2).astype(np.float32)
+    _route_case(50, 64, 8, lg, "deepseek_v3", np.zeros(64, np.float32), 8, 3, 1.0)
+
+
+def test_permute_is_an_exact_gather():
+    g = gpu_layer(NAMED_CONFIGS[2])
+    c = g.cfg
+    r = run_route(g)
+    d = ml.dims(c.T, c.H, c.I, c.E, c.top_k)
+    xp = torch.empty((c.R, c.H), dtype=torch.int16, device=dev())
+    ml.moe_lora_permute(d, g.x, torch.from_numpy(r["p2e"]).to(dev()), xp)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(xp), oracle.permute_rows(g.x_np, r["p2e"], c.top_k))
+
+
+def test_finalize_matches_oracle():
+    say("[finalize]")
+    rng = np.random.default_rng(1)
+    T, k, H = 301, 8, 2048 + 8
+    y = f32_to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    w = rng.random((T, k)).astype(np.float32)
+    e2p = rng.permutation(T * k).astype(np.int32)
+    d = ml.dims(T, H, 64, 16, k)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev())
+    ml.moe_lora_finalize(d, t16(y), torch.from_numpy(w).to(dev()), torch.from_numpy(e2p).to(dev()), out)
+    torch.cuda.synchronize()
+    ref = oracle.finalize(oracle.bf16_bits_to_f64(y), w.astype(np.float64), e2p)
+    got = f64(out)
+    # fp32 sum of 8 terms then one bf16 rounding: within one bf16 ulp of the fp64 sum
+    np.testing.assert_allclose(got, ref, rtol=2 ** -8, atol=1e-6)
+
+
+def _layer_case(g: GpuLayer, gather=True, token_slot=None, with_lora=True, side=None):
+    c = g.cfg
+    layer = g.layer(gather_on_load=gather)
+    lora = g.lora_slots(token_slot) if with_lora else None
+    out = layer(g.x, g.logits, lora, side_stream=side)
+    torch.cuda.synchronize()
+    return layer, lora, out.clone()
+
+
+def _oracle_out(g: GpuLayer, token_slot=None, with_lora=True):
+    c = g.cfg
+    ads = g.oracle_adapters() if with_lora else []
+    ts = g.slots_np if token_slot is None else token_slot
+    return oracle.layer(g.x_np, g.logits_np, c.top_k, c.I, g.w_gate_up, g.w_down, ads, ts, c.routing,
+                        g.bias_np, c.n_group, c.topk_group, c.routed_scaling_factor, num_experts=c.E)
+
+
+@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], RAGGED, NAMED_CONFIGS[2], NAMED_CONFIGS[4]],
+                         ids=lambda c: c.name)
+@pytest.mark.parametrize("with_lora", [True, False], ids=["lora", "base"])
+def test_layer_parity_full(cfg, with_lora):
+    g = gpu_layer(cfg)
+    say(f"[layer] {cfg.name} lora={with_lora}")
+    layer, lora, out = _layer_case(g, with_lora=with_lora)
+    ref = _oracle_out(g, with_lora=with_lora)
+    rt = layer.last_route(cfg.T, lora)
+    np.testing.assert_array_equal(rt.topk_ids.cpu().numpy(), ref["ids"])
+    np.testing.assert_array_equal(rt.p2e.cpu().numpy(), ref["p2e"])
+    assert_layer_close(f64(out), ref["out"], f"{cfg.name} lora={with_lora}")
+
+
+def test_layer_parity_ragged_invalid_and_empty_slots():
+    g = gpu_layer(RAGGED)
+    ts = g.slots_np.copy()
+    ts[::4] = -1
+    ts[1::7] = 11  # out of range -> no adapter
+    say("[layer] ragged with -1 / out-of-range slots")
+    _, _, out = _layer_case(g, token_slot=ts)
+    ref = _oracle_out(g, token_slot=ts)
+    assert_layer_close(f64(out), ref["out"], "ragged mixed slots")
+
+
+def test_zero_lora_is_bit_identical_to_base_path():
+    g = gpu_layer(NAMED_CONFIGS[4])
+    say("[layer] zero-B LoRA vs base")
+    layer = g.layer()
+    base = layer(g.x, g.logits, None).clone()
+    zb = layer(g.x, g.logits, g.lora_slots(zero_b=True)).clone()
+    nos = layer(g.x, g.logits, g.lora_slots(np.full(g.cfg.T, -1, np.int32))).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(base, zb)
+    assert torch.equal(base, nos)
+
+
+def test_gather_on_load_equals_permuted_input_and_is_deterministic():
+    g = gpu_layer(NAMED_CONFIGS[4])
+    say("[layer] gather vs permute, determinism")
+    _, _, a = _layer_case(g, gather=True)
+    _, _, b = _layer_case(g, gather=False)
+    _, _, c = _layer_case(g, gather=True)
+    assert torch.equal(a, b)
+    assert torch.equal(a, c)
+
+
+def test_layer_parity_prefill_sampled():
+    cfg = NAMED_CONFIGS[3]
+    g = gpu_layer(cfg)
+    say(f"[layer] {cfg.name}: routing on all tokens, output on sampled tokens")
+    layer, lora, out = _layer_case(g)
+    rt = layer.last_route(cfg.T, lora)
+    ids, w = g.oracle_route()
+    check_route({"ids": rt.topk_ids.cpu().numpy(), "w": rt.topk_weights.cpu().numpy(),
+                 "off": rt.expert_offsets.cpu().numpy(), "e2p": rt.e2p.cpu().numpy(),
+                 "p2e": rt.p2e.cpu().numpy()}, ids, w, cfg.E)
+    rng = np.random.default_rng(0)
+    toks = np.sort(np.concatenate([rng.choice(cfg.T, 200, replace=False), [0, cfg.T - 1]]))
+    ref = oracle.layer_sampled(g.x_np, ids, w, toks, cfg.I, g.w_gate_up, g.w_down, g.oracle_adapters(),
+                               g.slots_np)
+    assert_layer_close(f64(out)[toks], ref, "prefill sampled")
+
+
+def test_empty_batch():
+    g = gpu_layer(NAMED_CONFIGS[1])
+    c = g.cfg
+    layer = g.layer()
+    d = layer.dims(0)
+    off = torch.full((c.E + 1,), 7, dtype=torch.int32, device=dev())
+    e = torch.empty((0,), dtype=torch.int32, device=dev())
+    ml.moe_lora_route(d, g.logits[:0], e, torch.empty((0,), device=dev()), off, e, e, None)
+    torch.cuda.synchronize()
+    assert (off.cpu() == 0).all()
