@@ -77,6 +77,7 @@ int moe_lora_route(const moe_lora_dims *d, int routing, const moe_lora_grouped *
   if (routing != MOE_LORA_ROUTING_RENORMALIZE && routing != MOE_LORA_ROUTING_DEEPSEEK_V3)
     return MOE_LORA_ERR_INVALID_ARGUMENT;
   const int E = d->num_experts, K = d->top_k;
+  if (d->num_tokens > moe::route_max_tokens()) return MOE_LORA_ERR_UNSUPPORTED;
   moe::RouteArgs a{};
   if (routing == MOE_LORA_ROUTING_DEEPSEEK_V3) {
     if (!g) return MOE_LORA_ERR_INVALID_ARGUMENT;

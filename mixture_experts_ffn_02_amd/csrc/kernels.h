@@ -25,6 +25,7 @@ struct RouteArgs {
   int32_t *hist;  // workspace [num_wg][E]
 };
 int route_num_wg(int T);
+int route_max_tokens();
 int launch_route(const RouteArgs &a, hipStream_t s);
 int launch_zero_offsets(int32_t *offsets, int E, hipStream_t s);
 

@@ -1,20 +1,23 @@
-// Routing + expert-sorted pack in one cooperative launch (gfx950).
+// Routing + expert-sorted pack in one launch (gfx950).
 //
 // Pages: sglang PR "[LoRA] Experimental fast LoRA path ... FP8 and NVFP4 models",
 // Optimizations (top-k and the routed pack fused in one launch); vLLM API page
 // "trtllm_lora_moe" (routing methods Renormalize / DeepSeekV3 and their n_group,
 // topk_group, routed_scaling_factor arguments; expanded index = token*top_k + k).
 //
-// Phase 1 (one wavefront per token): each lane holds a contiguous run of EPL experts.
-//   Renormalize keys are 32-bit words (order-preserving bf16 bits << 16 | (0xffff - e)),
-//   so one wave max picks the largest logit and, among equal logits, the lower index.
-//   DeepSeek-V3 keys are fp64 (sigmoid + bias) compared lexicographically with the
-//   expert index.  Each workgroup accumulates a per-expert histogram in LDS.
-// grid.sync()
-// Phase 2: every workgroup derives the global expert offsets and its own base inside
-//   each expert from all histograms, then wave 0 scatters its expanded rows in order;
-//   the stable rank among equal experts inside a 64-row chunk comes from ballots over
-//   the bits of the expert id.
+// Phase 1 (one wavefront per token, tokens of a wave contiguous): each lane holds a
+//   contiguous run of EPL experts.  Renormalize keys are 32-bit words
+//   (order-preserving bf16 bits << 16 | (0xffff - e)), so one DPP wave max picks the
+//   largest logit and, among equal logits, the lower index.  DeepSeek-V3 keys are fp64
+//   (sigmoid + bias); their wave argmax compares the high 32 bits of the
+//   order-preserving 64-bit pattern with a DPP max, and only on a tie of those bits
+//   falls back to the low bits and then to the lower index, so the selection is exact.
+//   Each wave counts its experts in an LDS histogram row of its own.
+// Workgroups then agree on global offsets: a single workgroup (T <= 256) needs no
+//   grid-wide step; larger batches use a cooperative launch with one grid.sync().
+// Phase 2: every wave scatters its own contiguous run of expanded rows; the stable
+//   rank among equal experts inside a 64-row chunk comes from ballots over the bits of
+//   the expert id, the base from the per-wave, per-workgroup prefix counts.
 #include <hip/hip_cooperative_groups.h>
 
 #include "common.h"
@@ -25,9 +28,10 @@ namespace cg = cooperative_groups;
 namespace moe {
 namespace {
 
-constexpr int kRouteThreads = 512;
+constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
-constexpr int kMaxE = MOE_LORA_MAX_EXPERTS;
+constexpr int kSingleMaxT = 256;    // one workgroup handles the whole batch up to this
+constexpr int kMaxTokPerWg = 256;   // LDS bound of the per-workgroup id buffer
 
 struct RouteParams {
   RouteArgs a;
@@ -41,74 +45,87 @@ MOE_DEV uint32_t bf16_order_key(uint32_t b) {
   return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
 }
 
+MOE_DEV float order_key_to_f32(uint32_t o) {
+  const uint32_t b = (o & 0x8000u) ? (o & 0x7fffu) : (~o & 0xffffu);
+  return bf16_to_f32(b);
+}
+
+MOE_DEV uint64_t f64_order_key(double v) {
+  if (v == 0.0) v = 0.0;  // -0 == +0
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  return (u >> 63) ? ~u : (u | (1ull << 63));
+}
+
 MOE_DEV bool better(double va, int ia, double vb, int ib) { return va > vb || (va == vb && ia < ib); }
 
-MOE_DEV void wave_argmax(double &v, int &i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    double ov = __shfl_xor(v, off);
-    int oi = __shfl_xor(i, off);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
+MOE_DEV uint32_t wave_max_u32(uint32_t v) { return __reduce_max_sync(~0ull, v); }
+MOE_DEV int wave_min_i32(int v) { return __reduce_min_sync(~0ull, v); }
+
+// Exact wave argmax of (key desc, index asc) over lanes with valid == true; returns the
+// winning index (wave-uniform).  At least one lane must be valid.
+MOE_DEV int wave_argmax_f64(double key, int idx, bool valid) {
+  const uint64_t u = valid ? f64_order_key(key) : 0ull;
+  const uint32_t hi = (uint32_t)(u >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  uint64_t mask = __ballot(valid && hi == mh);
+  if (__popcll(mask) > 1) {
+    const bool in = valid && hi == mh;
+    const uint32_t lo = in ? (uint32_t)u : 0u;
+    const uint32_t ml = wave_max_u32(lo);
+    const bool in2 = in && lo == ml;
+    mask = __ballot(in2);
+    if (__popcll(mask) > 1) return wave_min_i32(in2 ? idx : 0x7fffffff);
   }
+  const int lane = __ffsll((unsigned long long)mask) - 1;
+  return __builtin_amdgcn_readlane(idx, lane);
 }
 
-MOE_DEV double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-// Renormalize: returns in lane j < K the j-th expert; fp64 softmax over the k logits.
+// Renormalize: lane j < K ends with the j-th expert and its weight (softmax over the k
+// selected logits, fp32).
 template <int EPL>
-MOE_DEV void topk_renormalize(const uint16_t *row, int E, int K, int lane, int &my_e, double &my_w) {
+MOE_DEV void topk_renormalize(const uint16_t (&v)[EPL], int E, int K, int lane, int &my_e,
+                              float &my_w) {
   uint32_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    int e = lane * EPL + i;
-    key[i] = (e < E) ? ((bf16_order_key(row[e]) << 16) | (0xffffu - (uint32_t)e)) : 0u;
+    const int e = lane * EPL + i;
+    key[i] = (e < E) ? ((bf16_order_key(v[i]) << 16) | (0xffffu - (uint32_t)e)) : 0u;
   }
   my_e = -1;
+  float my_l = 0.f, l0 = 0.f, sum = 0.f;
   for (int j = 0; j < K; ++j) {
     uint32_t best = key[0];
 #pragma unroll
     for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    const uint32_t m = wave_max_u32(best);
+    const int e = (int)(0xffffu - (m & 0xffffu));
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      uint32_t o = __shfl_xor(best, off);
-      best = o > best ? o : best;
+    for (int i = 0; i < EPL; ++i)
+      if (key[i] == m) key[i] = 0u;
+    const float l = order_key_to_f32(m >> 16);
+    if (j == 0) l0 = l;
+    sum += expf(l - l0);
+    if (lane == j) {
+      my_e = e;
+      my_l = l;
     }
-    int e = (int)(0xffffu - (best & 0xffffu));
-    if (lane == e / EPL) {
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (i == e % EPL) key[i] = 0u;
-    }
-    if (lane == j) my_e = e;
   }
-  double l = (my_e >= 0) ? (double)bf16_to_f32(row[my_e]) : 0.0;
-  double m = __shfl(l, 0);
-  double ex = (my_e >= 0) ? exp(l - m) : 0.0;
-  double sum = wave_sum(ex);
-  my_w = ex / sum;
+  my_w = (my_e >= 0) ? expf(my_l - l0) / sum : 0.f;
 }
 
-// DeepSeek-V3 grouped routing, keys in fp64.
+// DeepSeek-V3 grouped routing, keys in fp64 (selection); weights in fp32.
 template <int EPL>
-MOE_DEV void topk_dsv3(const uint16_t *row, const float *bias, int E, int K, int n_group,
+MOE_DEV void topk_dsv3(const uint16_t (&v)[EPL], const float *bias, int E, int K, int n_group,
                        int topk_group, float rsf, int lane, double *keys_lds, int &my_e,
-                       double &my_w) {
+                       float &my_w) {
   double key[EPL];
   int idx[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    int e = lane * EPL + i;
+    const int e = lane * EPL + i;
     if (e < E) {
-      double l = (double)bf16_to_f32(row[e]);
-      double s = 1.0 / (1.0 + exp(-l));
-      key[i] = s + (bias ? (double)bias[e] : 0.0);
+      const double l = (double)bf16_to_f32(v[i]);
+      key[i] = 1.0 / (1.0 + exp(-l)) + (bias ? (double)bias[e] : 0.0);
       idx[i] = e;
       keys_lds[e] = key[i];
     } else {
@@ -120,172 +137,209 @@ MOE_DEV void topk_dsv3(const uint16_t *row, const float *bias, int E, int K, int
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int per = E / n_group;
-  // group score: sum of the two largest keys of the group (one if the group has one)
+  // group score: sum of the two largest keys of the group (the key itself for one expert)
   double gv = -INFINITY;
-  int gi = 0x7fffffff;
   if (lane < n_group) {
     double b0 = -INFINITY, b1 = -INFINITY;
     for (int q = 0; q < per; ++q) {
-      double v = keys_lds[lane * per + q];
-      if (v > b0) {
+      const double x = keys_lds[lane * per + q];
+      if (x > b0) {
         b1 = b0;
-        b0 = v;
-      } else if (v > b1) {
-        b1 = v;
+        b0 = x;
+      } else if (x > b1) {
+        b1 = x;
       }
     }
     gv = per >= 2 ? b0 + b1 : b0;
-    gi = lane;
   }
+  __builtin_amdgcn_wave_barrier();
   uint64_t chosen = 0;
   for (int r = 0; r < topk_group; ++r) {
-    double v = gv;
-    int i = gi;
-    wave_argmax(v, i);
-    chosen |= 1ull << i;
-    if (lane == i) {
-      gv = -INFINITY;
-      gi = 0x7fffffff;
-    }
+    const bool valid = lane < n_group && !((chosen >> lane) & 1ull);
+    const int g = wave_argmax_f64(gv, lane, valid);
+    chosen |= 1ull << g;
   }
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    if (idx[i] != 0x7fffffff && !((chosen >> (idx[i] / per)) & 1ull)) {
-      key[i] = -INFINITY;
-      idx[i] = 0x7fffffff;
-    }
+    if (idx[i] != 0x7fffffff && !((chosen >> (idx[i] / per)) & 1ull)) idx[i] = 0x7fffffff;
   }
   my_e = -1;
+  float sum = 0.f, my_s = 0.f;
   for (int j = 0; j < K; ++j) {
-    double v = key[0];
-    int i0 = idx[0];
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 1; i < EPL; ++i)
-      if (better(key[i], idx[i], v, i0)) {
-        v = key[i];
-        i0 = idx[i];
+    for (int i = 0; i < EPL; ++i)
+      if (idx[i] != 0x7fffffff && (bi == 0x7fffffff || better(key[i], idx[i], bv, bi))) {
+        bv = key[i];
+        bi = idx[i];
       }
-    wave_argmax(v, i0);
-    if (lane == i0 / EPL) {
+    const int e = wave_argmax_f64(bv, bi, bi != 0x7fffffff);
 #pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (idx[i] == i0) {
-          key[i] = -INFINITY;
-          idx[i] = 0x7fffffff;
-        }
+    for (int i = 0; i < EPL; ++i)
+      if (idx[i] == e) idx[i] = 0x7fffffff;
+    int vb = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (i == e % EPL) vb = (int)v[i];
+    const float s = 1.0f / (1.0f + expf(-bf16_to_f32((uint32_t)__builtin_amdgcn_readlane(vb, e / EPL))));
+    sum += s;
+    if (lane == j) {
+      my_e = e;
+      my_s = s;
     }
-    if (lane == j) my_e = i0;
   }
-  double s = 0.0;
-  if (my_e >= 0) s = 1.0 / (1.0 + exp(-(double)bf16_to_f32(row[my_e])));
-  double sum = wave_sum(s);
-  my_w = (double)rsf * s / sum;
+  my_w = (my_e >= 0) ? rsf * my_s / sum : 0.f;
 }
 
 template <int EPL>
+MOE_DEV void load_row(const uint16_t *row, int E, int lane, uint16_t (&v)[EPL]) {
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane * EPL + i;
+    v[i] = (e < E) ? row[e] : (uint16_t)0;
+  }
+}
+
+// Dynamic LDS: hist_w [waves][E] int | ids [tok_per_wg*K] int | tot [E] | wgbase [E]
+//              | keys [waves][E] double (DeepSeek-V3 only)
+template <int EPL, bool COOP>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams P) {
   const RouteArgs &a = P.a;
-  __shared__ int32_t hist[kMaxE];
-  __shared__ int32_t start[kMaxE];
-  __shared__ double keys[kRouteWaves][kMaxE];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  for (int e = tid; e < a.E; e += kRouteThreads) hist[e] = 0;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int E = a.E, K = a.K;
+  int32_t *hist_w = reinterpret_cast<int32_t *>(smem);
+  int32_t *ids_l = hist_w + kRouteWaves * E;
+  int32_t *tot = ids_l + P.tok_per_wg * K;
+  int32_t *wgbase = tot + E;
+  double *keys = reinterpret_cast<double *>(
+      smem + (((size_t)(kRouteWaves * E + P.tok_per_wg * K + 2 * E) * 4 + 15) & ~(size_t)15));
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) hist_w[i] = 0;
   __syncthreads();
 
-  const int t0 = blockIdx.x * P.tok_per_wg;
-  const int t1 = min(a.T, t0 + P.tok_per_wg);
-  for (int t = t0 + wave; t < t1; t += kRouteWaves) {
-    const uint16_t *row = a.logits + (size_t)t * a.E;
+  const int t_begin = blockIdx.x * P.tok_per_wg;
+  const int t_end = min(a.T, t_begin + P.tok_per_wg);
+  const int tpw = (P.tok_per_wg + kRouteWaves - 1) / kRouteWaves;
+  const int w_begin = min(t_end, t_begin + wave * tpw);
+  const int w_end = min(t_end, w_begin + tpw);
+  const bool dsv3 = a.method == MOE_LORA_ROUTING_DEEPSEEK_V3;
+
+  // ---- phase 1: top-k per token
+  uint16_t cur[EPL], nxt[EPL];
+  if (w_begin < w_end) load_row<EPL>(a.logits + (size_t)w_begin * E, E, lane, cur);
+  for (int t = w_begin; t < w_end; ++t) {
+    if (t + 1 < w_end) load_row<EPL>(a.logits + (size_t)(t + 1) * E, E, lane, nxt);
     int my_e;
-    double my_w;
-    if (a.method == MOE_LORA_ROUTING_DEEPSEEK_V3)
-      topk_dsv3<EPL>(row, a.bias, a.E, a.K, a.n_group, a.topk_group, a.rsf, lane, keys[wave], my_e,
+    float my_w;
+    if (dsv3)
+      topk_dsv3<EPL>(cur, a.bias, E, K, a.n_group, a.topk_group, a.rsf, lane, keys + wave * E, my_e,
                      my_w);
     else
-      topk_renormalize<EPL>(row, a.E, a.K, lane, my_e, my_w);
-    if (lane < a.K) {
-      a.ids[(size_t)t * a.K + lane] = my_e;
-      a.weights[(size_t)t * a.K + lane] = (float)my_w;
-      atomicAdd(&hist[my_e], 1);
+      topk_renormalize<EPL>(cur, E, K, lane, my_e, my_w);
+    if (lane < K) {
+      a.ids[(size_t)t * K + lane] = my_e;
+      a.weights[(size_t)t * K + lane] = my_w;
+      ids_l[(t - t_begin) * K + lane] = my_e;
+      hist_w[wave * E + my_e] += 1;  // the k experts of one token are distinct
     }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) cur[i] = nxt[i];
   }
   __syncthreads();
-  for (int e = tid; e < a.E; e += kRouteThreads) a.hist[(size_t)blockIdx.x * a.E + e] = hist[e];
 
-  cg::this_grid().sync();
-
-  // per-expert totals and this workgroup's base inside each expert
-  for (int e = tid; e < a.E; e += kRouteThreads) {
-    int before = 0, total = 0;
-    for (int b = 0; b < P.num_wg; ++b) {
-      int h = a.hist[(size_t)b * a.E + e];
-      total += h;
-      before += (b < (int)blockIdx.x) ? h : 0;
+  // ---- per-expert counts of this workgroup, global totals and this workgroup's base
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int c = 0;
+    for (int w = 0; w < kRouteWaves; ++w) c += hist_w[w * E + e];
+    tot[e] = c;
+    if (COOP) a.hist[(size_t)blockIdx.x * E + e] = c;
+  }
+  if (COOP) {
+    cg::this_grid().sync();
+    for (int e = tid; e < E; e += kRouteThreads) {
+      int before = 0, total = 0;
+      for (int b = 0; b < P.num_wg; ++b) {
+        const int h = a.hist[(size_t)b * E + e];
+        total += h;
+        before += (b < (int)blockIdx.x) ? h : 0;
+      }
+      tot[e] = total;
+      wgbase[e] = before;
     }
-    hist[e] = total;
-    start[e] = before;
+  } else {
+    for (int e = tid; e < E; e += kRouteThreads) wgbase[e] = 0;
   }
   __syncthreads();
   if (wave == 0) {
-    // exclusive scan of the totals, EPL' consecutive experts per lane
-    const int per_lane = (a.E + 63) / 64;
+    // exclusive scan of the totals over experts, consecutive experts per lane
+    const int per_lane = (E + 63) / 64;
     int local = 0;
     for (int q = 0; q < per_lane; ++q) {
-      int e = lane * per_lane + q;
-      local += (e < a.E) ? hist[e] : 0;
+      const int e = lane * per_lane + q;
+      local += (e < E) ? tot[e] : 0;
     }
     int incl = local;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      int o = __shfl_up(incl, off);
+      const int o = __shfl_up(incl, off);
       if (lane >= off) incl += o;
     }
     int run = incl - local;
     for (int q = 0; q < per_lane; ++q) {
-      int e = lane * per_lane + q;
-      if (e < a.E) {
-        int c = hist[e];
+      const int e = lane * per_lane + q;
+      if (e < E) {
+        const int c = tot[e];
         if (blockIdx.x == 0) a.offsets[e] = run;
-        start[e] += run;
+        wgbase[e] += run;
         run += c;
       }
     }
-    if (blockIdx.x == 0 && lane == 63) a.offsets[a.E] = incl;
+    if (blockIdx.x == 0 && lane == 63) a.offsets[E] = incl;
+  }
+  __syncthreads();
+  // per-wave starting positions: offsets + workgroup base + earlier waves of this workgroup
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int run = wgbase[e];
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int c = hist_w[w * E + e];
+      hist_w[w * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: stable scatter of this wave's expanded rows
+  int32_t *start = hist_w + wave * E;
+  const int j0 = w_begin * K, j1 = w_end * K;
+  const int jl0 = t_begin * K;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = j0; base < j1; base += 64) {
+    const int j = base + lane;
+    const bool valid = j < j1;
+    const int e = valid ? ids_l[j - jl0] : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(valid && bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt);
+    int s = 0;
+    if (valid) s = start[e];
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      const int pos = s + rank;
+      a.e2p[j] = pos;
+      a.p2e[pos] = j;
+      if ((peers & lt) == 0ull) start[e] = s + __popcll(peers);
+    }
+    __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // stable scatter of this workgroup's expanded rows
-    const int j0 = t0 * a.K;
-    const int j1 = t1 * a.K;
-    int nbits = 0;
-    while ((1 << nbits) < a.E) ++nbits;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = j0; base < j1; base += 64) {
-      const int j = base + lane;
-      const bool valid = j < j1;
-      const int e = valid ? a.ids[j] : 0;
-      uint64_t peers = __ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t m = __ballot(valid && bit);
-        peers &= bit ? m : ~m;
-      }
-      const int rank = __popcll(peers & lt);
-      int s = 0;
-      if (valid) s = start[e];
-      __builtin_amdgcn_wave_barrier();
-      if (valid) {
-        const int pos = s + rank;
-        a.e2p[j] = pos;
-        a.p2e[pos] = j;
-        if ((peers & lt) == 0ull) start[e] = s + __popcll(peers);
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
   }
 }
 
@@ -293,54 +347,71 @@ __global__ void zero_offsets_kernel(int32_t *offsets, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) offsets[i] = 0;
 }
 
-struct CoopLimit {
-  int dev = -1;
-  int max_wg[4] = {0, 0, 0, 0};
-};
-
-template <int EPL>
-int max_coresident(int slot) {
-  static CoopLimit cache[16];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  CoopLimit &c = cache[dev & 15];
-  if (c.dev != dev || c.max_wg[slot] == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_kernel<EPL>, kRouteThreads, 0) !=
-        hipSuccess)
-      return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    c.dev = dev;
-    c.max_wg[slot] = per_cu * cus;
-  }
-  return c.max_wg[slot];
+size_t route_lds_bytes(int E, int K, int tok_per_wg, bool dsv3) {
+  size_t b = ((size_t)(kRouteWaves * E + tok_per_wg * K + 2 * E) * 4 + 15) & ~(size_t)15;
+  if (dsv3) b += (size_t)kRouteWaves * E * sizeof(double);
+  return b;
 }
 
 template <int EPL>
-int launch_epl(const RouteArgs &a, hipStream_t s, int slot) {
+int max_coresident(size_t lds) {
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_kernel<EPL, true>, kRouteThreads,
+                                                   lds) != hipSuccess)
+    return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return per_cu * cus;
+}
+
+template <int EPL, bool COOP>
+bool allow_lds(size_t lds) {
+  static size_t granted = 64 * 1024;
+  if (lds <= granted) return true;
+  if (hipFuncSetAttribute((const void *)route_kernel<EPL, COOP>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return false;
+  granted = lds;
+  return true;
+}
+
+template <int EPL>
+int launch_epl(const RouteArgs &a, hipStream_t s) {
   RouteParams P;
   P.a = a;
+  const bool dsv3 = a.method == MOE_LORA_ROUTING_DEEPSEEK_V3;
+  if (a.T <= kSingleMaxT) {
+    P.num_wg = 1;
+    P.tok_per_wg = a.T;
+    const size_t lds = route_lds_bytes(a.E, a.K, P.tok_per_wg, dsv3);
+    if (!allow_lds<EPL, false>(lds)) return ST_HIP;
+    route_kernel<EPL, false><<<1, kRouteThreads, lds, s>>>(P);
+    return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
+  }
   int nwg = route_num_wg(a.T);
-  int lim = max_coresident<EPL>(slot);
-  if (lim <= 0) return ST_HIP;
-  if (nwg > lim) nwg = lim;
   P.num_wg = nwg;
   P.tok_per_wg = (a.T + nwg - 1) / nwg;
+  const size_t lds = route_lds_bytes(a.E, a.K, P.tok_per_wg, dsv3);
+  if (!allow_lds<EPL, true>(lds)) return ST_HIP;
+  const int lim = max_coresident<EPL>(lds);
+  if (lim < nwg) return ST_UNSUPPORTED;
   void *args[] = {&P};
-  hipError_t err = hipLaunchCooperativeKernel((const void *)route_kernel<EPL>, dim3(nwg),
-                                              dim3(kRouteThreads), args, 0, s);
+  hipError_t err = hipLaunchCooperativeKernel((const void *)route_kernel<EPL, true>, dim3(nwg),
+                                              dim3(kRouteThreads), args, (unsigned)lds, s);
   return err == hipSuccess ? ST_OK : ST_HIP;
 }
 
 }  // namespace
 
 int route_num_wg(int T) {
+  if (T <= kSingleMaxT) return 1;
   int n = (T + 63) / 64;
-  if (n < 1) n = 1;
   if (n > 128) n = 128;
+  if ((T + n - 1) / n > kMaxTokPerWg) n = (T + kMaxTokPerWg - 1) / kMaxTokPerWg;
   return n;
 }
+
+int route_max_tokens() { return 256 * kMaxTokPerWg; }
 
 int launch_zero_offsets(int32_t *offsets, int E, hipStream_t s) {
   zero_offsets_kernel<<<1, 256, 0, s>>>(offsets, E + 1);
@@ -349,10 +420,10 @@ int launch_zero_offsets(int32_t *offsets, int E, hipStream_t s) {
 
 int launch_route(const RouteArgs &a, hipStream_t s) {
   const int need = (a.E + 63) / 64;
-  if (need <= 1) return launch_epl<1>(a, s, 0);
-  if (need <= 2) return launch_epl<2>(a, s, 1);
-  if (need <= 4) return launch_epl<4>(a, s, 2);
-  return launch_epl<8>(a, s, 3);
+  if (need <= 1) return launch_epl<1>(a, s);
+  if (need <= 2) return launch_epl<2>(a, s);
+  if (need <= 4) return launch_epl<4>(a, s);
+  return launch_epl<8>(a, s);
 }
 
 }  // namespace moe
