@@ -58,7 +58,7 @@ struct GemmParams {
   float *out_f32;
 };
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE, int PF>
 __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams P) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -70,6 +70,7 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
   constexpr bool kHasExt = (MODE == MODE_GATEUP || MODE == MODE_DOWN || MODE == MODE_EXPAND_F32);
   static_assert(FM >= 1 && FN >= 1, "wave tile too small");
   static_assert(!kGateUp || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
+  static_assert(PF >= 2 && PF % 2 == 0, "prefetch depth must be even (two LDS buffers)");
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDSP];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDSP];
@@ -142,50 +143,49 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
   __syncthreads();
   const int slot_mask = s_info[3];
 
-  // ---- per-thread chunk geometry (fixed for the whole K loop)
+  // ---- per-thread chunk geometry (fixed for the whole K loop).  Threads without a chunk,
+  // padding rows and weight rows past N read a valid row instead (never stored or masked
+  // out later), so the steady-state loads carry no predicate and stay in flight.
+  const int src0 = s_src[0];
   const uint16_t *a_ptr[A_IT];
   int a_lds[A_IT], a_row[A_IT], a_c8[A_IT];
+  bool a_has[A_IT];
 #pragma unroll
   for (int i = 0; i < A_IT; ++i) {
     const int c = tid + i * NT;
-    a_row[i] = -1;
-    a_ptr[i] = nullptr;
-    a_lds[i] = 0;
-    a_c8[i] = c & 7;
-    if (c < A_CH) {
-      const int r = c >> 3;
-      a_row[i] = r;
-      a_lds[i] = r * LDSP + (c & 7) * 8;
-      const int src = s_src[r];
-      if (src >= 0 && kHasMain && MODE != MODE_EXPAND_F32)
-        a_ptr[i] = P.a + (size_t)src * P.K + (c & 7) * 8;
-    }
+    const int cc = c < A_CH ? c : c % A_CH;
+    const int r = cc >> 3;
+    a_has[i] = c < A_CH;
+    a_row[i] = r;
+    a_c8[i] = cc & 7;
+    a_lds[i] = r * LDSP + (cc & 7) * 8;
+    const int src = s_src[r] >= 0 ? s_src[r] : src0;
+    a_ptr[i] = (kHasMain && src >= 0) ? P.a + (size_t)src * P.K + (cc & 7) * 8 : nullptr;
   }
   int b_wrow[B_IT], b_lds[B_IT], b_c8[B_IT];
+  bool b_has[B_IT];
 #pragma unroll
   for (int i = 0; i < B_IT; ++i) {
     const int c = tid + i * NT;
-    b_wrow[i] = -1;
-    b_lds[i] = 0;
-    b_c8[i] = c & 7;
-    if (c < B_CH) {
-      const int n = c >> 3;
-      b_lds[i] = n * LDSP + (c & 7) * 8;
-      if (MODE == MODE_SHRINK) {
-        b_wrow[i] = n;  // rank row, checked against the slot's rank
-      } else if (kGateUp) {
-        const int wnn = n / WTN, cc = n % WTN;
-        const int half = cc / (WTN / 2), j = cc % (WTN / 2);
-        const int icol = col * (BN / 2) + wnn * (WTN / 2) + j;
-        b_wrow[i] = (icol < P.I) ? half * P.I + icol : -1;
-      } else {
-        const int ng = col * BN + n;
-        b_wrow[i] = (ng < P.N) ? ng : -1;
-      }
+    const int cc = c < B_CH ? c : c % B_CH;
+    const int n = cc >> 3;
+    b_has[i] = c < B_CH;
+    b_c8[i] = cc & 7;
+    b_lds[i] = n * LDSP + (cc & 7) * 8;
+    if (MODE == MODE_SHRINK) {
+      b_wrow[i] = n;  // rank row, checked against the slot's rank
+    } else if (kGateUp) {
+      const int wnn = n / WTN, ccw = n % WTN;
+      const int half = ccw / (WTN / 2), j = ccw % (WTN / 2);
+      const int icol = col * (BN / 2) + wnn * (WTN / 2) + j;
+      b_wrow[i] = (icol < P.I) ? half * P.I + icol : -1;
+    } else {
+      const int ng = col * BN + n;
+      b_wrow[i] = (ng < P.N) ? ng : -1;
     }
   }
 
-  u32x4_t ra[A_IT], rb[B_IT];
+  u32x4_t ra[PF][A_IT], rb[PF][B_IT];
   f32x4_t acc[FM][FN];
 
   auto zero_acc = [&]() {
@@ -195,39 +195,52 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
 
-  // main K step: A rows and B (= W or the slot's LoRA A) rows from global memory
-  auto load_main = [&](int k0, const uint16_t *bbase, int bcount) {
+  // full 64-wide K step, no predicates (see above)
+  auto load_full = [&](int k0, const uint16_t *bbase, int bcount, u32x4_t(&xa)[A_IT],
+                       u32x4_t(&xb)[B_IT]) {
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) xa[i] = *reinterpret_cast<const u32x4_t *>(a_ptr[i] + k0);
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+      const int wr = (b_wrow[i] >= 0 && b_wrow[i] < bcount) ? b_wrow[i] : 0;
+      xb[i] = *reinterpret_cast<const u32x4_t *>(bbase + (size_t)wr * P.K + k0 + b_c8[i] * 8);
+    }
+  };
+  // ragged K tail and padding rows zeroed (used once, off the steady state)
+  auto load_tail = [&](int k0, const uint16_t *bbase, int bcount, u32x4_t(&xa)[A_IT],
+                       u32x4_t(&xb)[B_IT]) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
-      ra[i] = zero_u32x4();
-      if (a_ptr[i] && k0 + a_c8[i] * 8 < P.K) ra[i] = *reinterpret_cast<const u32x4_t *>(a_ptr[i] + k0);
+      xa[i] = zero_u32x4();
+      if (a_ptr[i] && a_row[i] < rows && k0 + a_c8[i] * 8 < P.K)
+        xa[i] = *reinterpret_cast<const u32x4_t *>(a_ptr[i] + k0);
     }
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
-      rb[i] = zero_u32x4();
+      xb[i] = zero_u32x4();
       const int wr = b_wrow[i];
       if (wr >= 0 && wr < bcount && k0 + b_c8[i] * 8 < P.K)
-        rb[i] = *reinterpret_cast<const u32x4_t *>(bbase + (size_t)wr * P.K + k0 + b_c8[i] * 8);
+        xb[i] = *reinterpret_cast<const u32x4_t *>(bbase + (size_t)wr * P.K + k0 + b_c8[i] * 8);
     }
   };
 
   // LoRA expand step for slot a: A = bf16(s_a * sum of partials) on rows of that slot,
   // B = B_lora[a][e] rows (rank columns), zero beyond the rank.
-  auto load_ext = [&](int a) {
+  auto load_ext = [&](int a, u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
     const int ra_rank = P.rank[a];
     const float sc = P.scaling[a];
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
-      ra[i] = zero_u32x4();
+      xa[i] = zero_u32x4();
       const int r = a_row[i];
       const int j0 = a_c8[i] * 8;
-      if (r >= 0 && j0 < ra_rank && s_slot[r] == a) {
+      if (j0 < ra_rank && s_slot[r] == a) {
         const int p = row0 + r;
         float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < P.part_splits; ++s) {
-          const f32x4_t *src =
-              reinterpret_cast<const f32x4_t *>(P.part + ((size_t)s * P.R + p) * P.rmax + j0);
-          const f32x4_t x0 = src[0], x1 = src[1];
+        for (int sp = 0; sp < P.part_splits; ++sp) {
+          const f32x4_t *srcp =
+              reinterpret_cast<const f32x4_t *>(P.part + ((size_t)sp * P.R + p) * P.rmax + j0);
+          const f32x4_t x0 = srcp[0], x1 = srcp[1];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             v[q] += x0[q];
@@ -238,39 +251,39 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
         for (int q = 0; q < 4; ++q) {
           const float lo = (j0 + 2 * q < ra_rank) ? v[2 * q] * sc : 0.f;
           const float hi = (j0 + 2 * q + 1 < ra_rank) ? v[2 * q + 1] * sc : 0.f;
-          ra[i][q] = pack_bf16x2(lo, hi);
+          xa[i][q] = pack_bf16x2(lo, hi);
         }
       }
     }
     const uint16_t *bl = P.lora_w[a];
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
-      rb[i] = zero_u32x4();
+      xb[i] = zero_u32x4();
       const int wr = b_wrow[i];
       const int j0 = b_c8[i] * 8;
       if (wr >= 0 && j0 < ra_rank) {
-        const uint16_t *src = bl + ((size_t)e * P.N + wr) * ra_rank + j0;
+        const uint16_t *srcb = bl + ((size_t)e * P.N + wr) * ra_rank + j0;
         if ((ra_rank & 7) == 0) {
-          rb[i] = *reinterpret_cast<const u32x4_t *>(src);
+          xb[i] = *reinterpret_cast<const u32x4_t *>(srcb);
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = (j0 + 2 * q < ra_rank) ? src[2 * q] : 0u;
-            const uint32_t hi = (j0 + 2 * q + 1 < ra_rank) ? src[2 * q + 1] : 0u;
-            rb[i][q] = lo | (hi << 16);
+            const uint32_t lo = (j0 + 2 * q < ra_rank) ? srcb[2 * q] : 0u;
+            const uint32_t hi = (j0 + 2 * q + 1 < ra_rank) ? srcb[2 * q + 1] : 0u;
+            xb[i][q] = lo | (hi << 16);
           }
         }
       }
     }
   };
 
-  auto store_lds = [&](int buf) {
+  // threads past the chunk count hold a duplicate of another thread's chunk, so every
+  // thread stores unconditionally (identical values to the same address)
+  auto store_lds = [&](int buf, const u32x4_t(&xa)[A_IT], const u32x4_t(&xb)[B_IT]) {
 #pragma unroll
-    for (int i = 0; i < A_IT; ++i)
-      if (a_row[i] >= 0) *reinterpret_cast<u32x4_t *>(&As[buf][a_lds[i]]) = ra[i];
+    for (int i = 0; i < A_IT; ++i) *reinterpret_cast<u32x4_t *>(&As[buf][a_lds[i]]) = xa[i];
 #pragma unroll
-    for (int i = 0; i < B_IT; ++i)
-      if (tid + i * NT < B_CH) *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = rb[i];
+    for (int i = 0; i < B_IT; ++i) *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = xb[i];
   };
 
   auto compute = [&](int buf) {
@@ -292,25 +305,65 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
     }
   };
 
+  // Full K steps [s_begin, s_end): PF register stages in flight, two LDS buffers, one
+  // barrier per step.  The steady-state loop has no branches between a load and the use
+  // of its registers.
+  auto run_full = [&](int s_begin, int s_end, const uint16_t *bbase, int bcount) {
+    const int n = s_end - s_begin;
+    const int n_main = (n / PF) * PF;
+    if (n_main > 0) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) load_full((s_begin + u) * BK, bbase, bcount, ra[u], rb[u]);
+      store_lds(0, ra[0], rb[0]);
+      __syncthreads();
+      for (int i = 0; i < n_main - PF; i += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          load_full((s_begin + i + u + PF) * BK, bbase, bcount, ra[u], rb[u]);
+          compute(u & 1);
+          store_lds((u + 1) & 1, ra[(u + 1) % PF], rb[(u + 1) % PF]);
+          __syncthreads();
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        compute(u & 1);
+        if (u + 1 < PF) store_lds((u + 1) & 1, ra[u + 1], rb[u + 1]);
+        __syncthreads();
+      }
+    }
+    for (int s = s_begin + n_main; s < s_end; ++s) {
+      load_full(s * BK, bbase, bcount, ra[0], rb[0]);
+      store_lds(0, ra[0], rb[0]);
+      __syncthreads();
+      compute(0);
+      __syncthreads();
+    }
+  };
+
+  auto run_single = [&](auto &&loader) {
+    loader(ra[0], rb[0]);
+    store_lds(0, ra[0], rb[0]);
+    __syncthreads();
+    compute(0);
+    __syncthreads();
+  };
+
   if constexpr (MODE == MODE_SHRINK) {
     const int steps_total = (P.K + BK - 1) / BK;
+    const int full_total = P.K / BK;
     const int s0 = col * P.k_steps_per_split;
     const int s1 = min(steps_total, s0 + P.k_steps_per_split);
+    const int s1f = min(s1, full_total);
     for (int a = 0; a < P.num_slots; ++a) {
       if (!((slot_mask >> a) & 1)) continue;
       const int r_a = P.rank[a];
       const uint16_t *bbase = P.lora_w[a] + (size_t)e * r_a * P.K;
       zero_acc();
-      load_main(s0 * BK, bbase, r_a);
-      store_lds(0);
-      __syncthreads();
-      for (int s = s0; s < s1; ++s) {
-        const int cur = (s - s0) & 1;
-        if (s + 1 < s1) load_main((s + 1) * BK, bbase, r_a);
-        compute(cur);
-        if (s + 1 < s1) store_lds(cur ^ 1);
-        __syncthreads();
-      }
+      run_full(s0, s1f, bbase, r_a);
+      if (s1 > s1f) run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
+        load_tail(s1f * BK, bbase, r_a, xa, xb);
+      });
       // rows of this slot, rank columns
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -326,31 +379,22 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
     }
     return;
   } else {
-    const int main_steps = kHasMain ? (P.K + BK - 1) / BK : 0;
-    const int n_ext = kHasExt ? __popc(slot_mask) : 0;
-    const int nsteps = main_steps + n_ext;
     const uint16_t *wbase = kHasMain ? P.w + (size_t)e * P.N * P.K : nullptr;
     const int wcount = kGateUp ? 2 * P.I : P.N;
-    auto load_step = [&](int s) {
-      if (s < main_steps) {
-        load_main(s * BK, wbase, wcount);
-      } else {
-        int m = slot_mask;
-        for (int q = 0; q < s - main_steps; ++q) m &= m - 1;
-        load_ext(__ffs(m) - 1);
-      }
-    };
     zero_acc();
-    if (nsteps > 0) {
-      load_step(0);
-      store_lds(0);
-      __syncthreads();
-      for (int s = 0; s < nsteps; ++s) {
-        const int cur = s & 1;
-        if (s + 1 < nsteps) load_step(s + 1);
-        compute(cur);
-        if (s + 1 < nsteps) store_lds(cur ^ 1);
-        __syncthreads();
+    if (kHasMain) {
+      const int full = P.K / BK;
+      run_full(0, full, wbase, wcount);
+      if (full * BK < P.K) run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
+        load_tail(full * BK, wbase, wcount, xa, xb);
+      });
+    }
+    if (kHasExt) {
+      int m = slot_mask;
+      while (m) {
+        const int a = __ffs(m) - 1;
+        m &= m - 1;
+        run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) { load_ext(a, xa, xb); });
       }
     }
 
@@ -388,6 +432,274 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
           }
     }
   }
+}
+
+// ---------------------------------------------------------------- weight-streaming variant
+// Decode-sized tiles (BM <= 32 token rows): every weight element is used by one MFMA
+// row block only, so staging it through LDS buys nothing.  Each wavefront owns 32 weight
+// rows (two 16-row MFMA fragments; for gate_up: 16 gate rows and the 16 matching up rows)
+// and streams them straight from HBM into registers in MFMA operand layout, keeping
+// PF K-steps of loads in flight.  The few token rows are read the same way (they stay in
+// L1/L2, shared by the wavefronts of the block).  No LDS, no barriers: wavefronts run
+// independently, which is what keeps enough bytes in flight to approach HBM bandwidth.
+
+// Per-wave lookup of (expert, first row, rows) for m-tile mt; returns false past the end.
+template <int BM>
+MOE_DEV bool find_tile(const GemmParams &P, int mt, int lane, int &e_out, int &row0, int &rows) {
+  const int per = (P.E + 63) / 64;
+  int local = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = lane * per + q;
+    if (e < P.E) local += (P.offsets[e + 1] - P.offsets[e] + BM - 1) / BM;
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  int run = incl - local;
+  int found = -1, f_row0 = 0, f_rows = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = lane * per + q;
+    if (e < P.E) {
+      const int lo = P.offsets[e], cnt = P.offsets[e + 1] - lo;
+      const int tiles = (cnt + BM - 1) / BM;
+      if (mt >= run && mt < run + tiles) {
+        found = e;
+        f_row0 = lo + (mt - run) * BM;
+        f_rows = min(BM, cnt - (mt - run) * BM);
+      }
+      run += tiles;
+    }
+  }
+  const uint64_t m = __ballot(found >= 0);
+  if (m == 0ull) return false;
+  const int src = __ffsll((unsigned long long)m) - 1;
+  e_out = __builtin_amdgcn_readlane(found, src);
+  row0 = __builtin_amdgcn_readlane(f_row0, src);
+  rows = __builtin_amdgcn_readlane(f_rows, src);
+  return true;
+}
+
+template <int BM, int NW, int MODE>
+__global__ __launch_bounds__(NW * 64) void moe_wstream_kernel(const GemmParams P) {
+  constexpr int FM = BM / 16;
+  constexpr int FN = 2;
+  constexpr int BN = NW * 32;
+  constexpr int PF = 4;
+  constexpr bool kGateUp = (MODE == MODE_GATEUP);
+  static_assert(MODE == MODE_GATEUP || MODE == MODE_DOWN, "streaming variant serves the two GEMMs");
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = gridDim.x;
+  const int bid = blockIdx.x;
+  const int L = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int mt = L / P.n_cols, col = L % P.n_cols;
+  int e, row0, rows;
+  if (!find_tile<BM>(P, mt, lane, e, row0, rows)) return;
+
+  const int lr = lane & 15;       // fragment row / column owned by this lane
+  const int kq = (lane >> 4) * 8; // K offset of this lane inside a 32-wide K slab
+
+  // token rows of this lane (one per 16-row fragment).  Rows past the tile end and weight
+  // rows past N point at a valid row instead (their results are never stored), so the
+  // steady-state loads carry no predicate and the compiler can keep PF steps in flight.
+  const uint16_t *a_ptr[FM];
+  int a_slot[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int r = min(fm * 16 + lr, rows - 1);
+    const int p = row0 + r;
+    const bool need_tok = P.a_gather || P.num_slots > 0;
+    const int tok = need_tok ? P.p2e[p] / P.top_k : 0;
+    a_ptr[fm] = P.a + (size_t)(P.a_gather ? tok : p) * P.K + kq;
+    a_slot[fm] = -1;
+    if (P.num_slots > 0 && fm * 16 + lr < rows) {
+      const int s = P.token_slot[tok];
+      a_slot[fm] = (s >= 0 && s < P.num_slots) ? s : -1;
+    }
+  }
+  // weight rows of this lane (one per fragment)
+  int wrow[FN];
+  const uint16_t *w_ptr[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    int wr;
+    if (kGateUp) {
+      const int icol = col * (BN / 2) + wave * 16 + lr;
+      wr = (icol < P.I) ? f * P.I + icol : -1;
+    } else {
+      const int n = col * BN + wave * 32 + f * 16 + lr;
+      wr = (n < P.N) ? n : -1;
+    }
+    wrow[f] = wr;
+    w_ptr[f] = P.w + ((size_t)e * P.N + (wr >= 0 ? wr : 0)) * P.K + kq;
+  }
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int f = 0; f < FN; ++f) acc[fm][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nfull = P.K / 64;  // full 64-wide K steps
+  u32x4_t wa[PF][FM][2], wb[PF][FN][2];
+  auto load_step = [&](int s, u32x4_t (&ra)[FM][2], u32x4_t (&rb)[FN][2]) {
+    const int k0 = s * 64;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        ra[fm][kk] = *reinterpret_cast<const u32x4_t *>(a_ptr[fm] + k0 + kk * 32);
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+        rb[f][kk] = *reinterpret_cast<const u32x4_t *>(w_ptr[f] + k0 + kk * 32);
+    }
+  };
+  // steady state: PF steps in flight, no branches between the loads and their use
+  const int nmain = (nfull / PF) * PF;
+  if (nmain > 0) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load_step(u, wa[u], wb[u]);
+    for (int s0 = 0; s0 < nmain - PF; s0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int f = 0; f < FN; ++f)
+              acc[fm][f] = mfma_16x16x32(wa[u][fm][kk], wb[u][f][kk], acc[fm][f]);
+        load_step(s0 + u + PF, wa[u], wb[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+            acc[fm][f] = mfma_16x16x32(wa[u][fm][kk], wb[u][f][kk], acc[fm][f]);
+  }
+  for (int s = nmain; s < nfull; ++s) {  // remaining full steps
+    load_step(s, wa[0], wb[0]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int f = 0; f < FN; ++f) acc[fm][f] = mfma_16x16x32(wa[0][fm][kk], wb[0][f][kk], acc[fm][f]);
+  }
+  if (nfull * 64 < P.K) {  // ragged K tail: zero the chunks past K
+    const int k0 = nfull * 64;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bool kin = k0 + kk * 32 + kq < P.K;
+      u32x4_t ra[FM], rb[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        ra[fm] = kin ? *reinterpret_cast<const u32x4_t *>(a_ptr[fm] + k0 + kk * 32) : zero_u32x4();
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+        rb[f] = kin ? *reinterpret_cast<const u32x4_t *>(w_ptr[f] + k0 + kk * 32) : zero_u32x4();
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int f = 0; f < FN; ++f) acc[fm][f] = mfma_16x16x32(ra[fm], rb[f], acc[fm][f]);
+    }
+  }
+
+  // LoRA expand: one 64-wide K step per slot present in the tile
+  if (P.num_slots > 0) {
+    int mask = 0;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      if (a_slot[fm] >= 0) mask |= 1 << a_slot[fm];
+    mask = __reduce_or_sync(~0ull, mask);
+    while (mask) {
+      const int a = __ffs(mask) - 1;
+      mask &= mask - 1;
+      const int ra_rank = P.rank[a];
+      const float sc = P.scaling[a];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int j0 = kk * 32 + kq;
+        u32x4_t ax[FM], bx[FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          ax[fm] = zero_u32x4();
+          if (a_slot[fm] == a && j0 < ra_rank) {
+            const int p = row0 + fm * 16 + lr;
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int sp = 0; sp < P.part_splits; ++sp) {
+              const f32x4_t *src =
+                  reinterpret_cast<const f32x4_t *>(P.part + ((size_t)sp * P.R + p) * P.rmax + j0);
+              const f32x4_t x0 = src[0], x1 = src[1];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[q] += x0[q];
+                v[4 + q] += x1[q];
+              }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float lo = (j0 + 2 * q < ra_rank) ? v[2 * q] * sc : 0.f;
+              const float hi = (j0 + 2 * q + 1 < ra_rank) ? v[2 * q + 1] * sc : 0.f;
+              ax[fm][q] = pack_bf16x2(lo, hi);
+            }
+          }
+        }
+        const uint16_t *bl = P.lora_w[a];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          bx[f] = zero_u32x4();
+          if (wrow[f] >= 0 && j0 < ra_rank) {
+            const uint16_t *src = bl + ((size_t)e * P.N + wrow[f]) * ra_rank + j0;
+            if ((ra_rank & 7) == 0) {
+              bx[f] = *reinterpret_cast<const u32x4_t *>(src);
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = (j0 + 2 * q < ra_rank) ? src[2 * q] : 0u;
+                const uint32_t hi = (j0 + 2 * q + 1 < ra_rank) ? src[2 * q + 1] : 0u;
+                bx[f][q] = lo | (hi << 16);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int f = 0; f < FN; ++f) acc[fm][f] = mfma_16x16x32(ax[fm], bx[f], acc[fm][f]);
+      }
+    }
+  }
+
+  // epilogue
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = fm * 16 + (lane >> 4) * 4 + i;
+      if (r >= rows) continue;
+      if (kGateUp) {
+        const int icol = col * (BN / 2) + wave * 16 + lr;
+        if (icol < P.I) {
+          const float g = acc[fm][0][i], u = acc[fm][1][i];
+          P.out_bf16[(size_t)(row0 + r) * P.I + icol] = (uint16_t)f32_to_bf16(g / (1.0f + expf(-g)) * u);
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int n = col * BN + wave * 32 + f * 16 + lr;
+          if (n < P.N) P.out_bf16[(size_t)(row0 + r) * P.N + n] = (uint16_t)f32_to_bf16(acc[fm][f][i]);
+        }
+      }
+    }
 }
 
 // ---------------------------------------------------------------- host side
@@ -430,7 +742,7 @@ int rmax8(const moe_lora_adapters *lora) {
   return (r + 7) & ~7;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE, int PF>
 int launch_cfg(const GemmParams &P, int n_cols, hipStream_t s) {
   int tiles = mtile_bound(P.R, P.E, BM);
   long long blocks = (long long)tiles * n_cols;
@@ -438,7 +750,20 @@ int launch_cfg(const GemmParams &P, int n_cols, hipStream_t s) {
   if (blocks == 0) return ST_OK;
   GemmParams Q = P;
   Q.n_cols = n_cols;
-  moe_gemm_kernel<BM, BN, WM, WN, MODE><<<dim3((unsigned)blocks), dim3(WM * WN * 64), 0, s>>>(Q);
+  moe_gemm_kernel<BM, BN, WM, WN, MODE, PF><<<dim3((unsigned)blocks), dim3(WM * WN * 64), 0, s>>>(Q);
+  return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
+}
+
+template <int BM, int NW, int MODE>
+int launch_stream(const GemmParams &P, hipStream_t s) {
+  constexpr int BN = NW * 32;
+  const int ncols = (MODE == MODE_GATEUP) ? cdiv(P.I, BN / 2) : cdiv(P.N, BN);
+  int tiles = mtile_bound(P.R, P.E, BM);
+  long long blocks = ((long long)tiles * ncols + 7) & ~7ll;
+  if (blocks == 0) return ST_OK;
+  GemmParams Q = P;
+  Q.n_cols = ncols;
+  moe_wstream_kernel<BM, NW, MODE><<<dim3((unsigned)blocks), dim3(NW * 64), 0, s>>>(Q);
   return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
 }
 
@@ -447,16 +772,16 @@ int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
   const int BN = 128;
   const int ncols = (MODE == MODE_GATEUP) ? cdiv(P.I, BN / 2) : cdiv(P.N, BN);
   switch (bm) {
-    case 16: return launch_cfg<16, 128, 1, 4, MODE>(P, ncols, s);
-    case 32: return launch_cfg<32, 128, 1, 4, MODE>(P, ncols, s);
-    case 64: return launch_cfg<64, 128, 2, 2, MODE>(P, ncols, s);
-    default: return launch_cfg<128, 128, 2, 2, MODE>(P, ncols, s);
+    case 16: return launch_cfg<16, 128, 1, 4, MODE, 4>(P, ncols, s);
+    case 32: return launch_cfg<32, 128, 1, 4, MODE, 4>(P, ncols, s);
+    case 64: return launch_cfg<64, 128, 2, 2, MODE, 2>(P, ncols, s);
+    default: return launch_cfg<128, 128, 2, 2, MODE, 2>(P, ncols, s);
   }
 }
 
 int launch_shrink(const GemmParams &P, int bm, int splits, hipStream_t s) {
-  if (bm <= 32) return launch_cfg<32, 64, 2, 2, MODE_SHRINK>(P, splits, s);
-  return launch_cfg<128, 64, 2, 2, MODE_SHRINK>(P, splits, s);
+  if (bm <= 32) return launch_cfg<32, 64, 2, 2, MODE_SHRINK, 2>(P, splits, s);
+  return launch_cfg<128, 64, 2, 2, MODE_SHRINK, 2>(P, splits, s);
 }
 
 struct FwdLayout {
