@@ -192,6 +192,19 @@ def main():
     t_off, gate_up_off_ms = timed(layer, None, args.steps, args.warmup, gate_up_events=True)
     log("timing LoRA on with the explicit permute call")
     t_perm, _ = timed(layer_p, lora, max(5, args.steps // 2), 3)
+    t_two = None
+    if lora is not None and cfg.T <= 256:
+        log("timing LoRA on, two-stream decomposed path")
+        side = torch.cuda.Stream()
+        for _ in range(args.warmup):
+            layer(x, logits, lora, side_stream=side)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n2 = max(5, args.steps // 2)
+        for _ in range(n2):
+            layer(x, logits, lora, side_stream=side)
+        torch.cuda.synchronize()
+        t_two = (time.perf_counter() - t0) / n2
 
     # realized routing -> algorithmic bytes and flops
     layer(x, logits, lora)
@@ -256,6 +269,7 @@ def main():
         "lora_ratio": round(tok_on / tok_off, 4),
         "ms_per_step_lora_off": round(t_off * 1e3, 4),
         "ms_per_step_explicit_permute": round(t_perm * 1e3, 4),
+        "ms_per_step_two_stream": round(t_two * 1e3, 4) if t_two else None,
         "layer_roofline": {
             "algorithmic_bytes": int(layer_bytes), "algorithmic_flops": int(layer_flops),
             "active_experts": active,

@@ -164,11 +164,19 @@ int moe_lora_permute(const moe_lora_dims *dims, const uint16_t *x,
  *   w_gate_up [E, 2I, H] (rows [0,I) gate, [I,2I) up), w_down [E, H, I]
  *   lora    NULL or num_slots == 0 -> the base MoE (same kernels, no LoRA work)
  *   y_perm  [T*k, H] output
- *   side    optional second stream: the gate_up LoRA runs there, overlapped with the
- *           base gate_up GEMM, and main waits on it before the activation; on return
- *           all work is ordered before later work on `main`.  NULL = one stream.
- *   opts    NULL = defaults.
- * Workspace: moe_lora_forward_workspace_size(dims, lora) bytes. */
+ *   side    optional second stream.  With LoRA and T <= two_stream_max_tokens (default and
+ *           maximum 256) the layer takes the decomposed path of the bf16 PR's two-stream
+ *           flow: the gate_up LoRA shrink and expand (delta) run on `side` while `main`
+ *           runs the base gate_up GEMM; `main` waits on the library's lora_ready event
+ *           right before the activation kernel, the delta's only consumer.  On return all
+ *           work is ordered before later work on `main`.  NULL = one stream: the fused
+ *           path (LoRA expand appended to the GEMM's K loop, SwiGLU in its epilogue).
+ *   opts    NULL = defaults.  force_path = 1 forces the fused path, 2 the decomposed path
+ *           (on one stream when side is NULL; MOE_LORA_ERR_UNSUPPORTED when T > 256).
+ * Workspace: moe_lora_forward_workspace_size(dims, lora) bytes; it includes the
+ * decomposed path's fp32 buffers when LoRA is present and T <= 256.
+ * Concurrency: the fork/join events are per device and shared by all calls; calls that
+ * use a side stream must not run concurrently on one device from several host threads. */
 size_t moe_lora_forward_workspace_size(const moe_lora_dims *dims, const moe_lora_adapters *lora);
 int moe_lora_forward(const moe_lora_dims *dims, const uint16_t *x, const uint16_t *x_perm,
                      const int32_t *expert_offsets, const int32_t *permuted_to_expanded,

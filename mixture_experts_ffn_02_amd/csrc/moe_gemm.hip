@@ -784,9 +784,60 @@ int launch_shrink(const GemmParams &P, int bm, int splits, hipStream_t s) {
   return launch_cfg<128, 64, 2, 2, MODE_SHRINK, 2>(P, splits, s);
 }
 
+// Activation of the decomposed path: act = silu(G_gate + D_gate) * (G_up + D_up), the
+// gate_up LoRA delta D joined right before SwiGLU (bf16 PR, Files-changed table,
+// activation row: the delta is added before SwiGLU; the activation output feeds the
+// down LoRA).  G and D are fp32 [R, 2I] with rows [gate | up]; one thread per 4 columns.
+__global__ __launch_bounds__(256) void swiglu_join_kernel(const float *__restrict__ G,
+                                                          const float *__restrict__ D,
+                                                          uint16_t *__restrict__ act, int R, int I) {
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = I / 4;
+  if (q >= (long long)R * per_row) return;
+  const int p = (int)(q / per_row), i = (int)(q % per_row) * 4;
+  const float *gr = G + (size_t)p * 2 * I, *dr = D + (size_t)p * 2 * I;
+  const f32x4_t g = *reinterpret_cast<const f32x4_t *>(gr + i);
+  const f32x4_t u = *reinterpret_cast<const f32x4_t *>(gr + I + i);
+  const f32x4_t dg = *reinterpret_cast<const f32x4_t *>(dr + i);
+  const f32x4_t du = *reinterpret_cast<const f32x4_t *>(dr + I + i);
+  float h[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float gg = g[c] + dg[c], uu = u[c] + du[c];
+    h[c] = gg / (1.0f + expf(-gg)) * uu;
+  }
+  uint2 o;
+  o.x = pack_bf16x2(h[0], h[1]);
+  o.y = pack_bf16x2(h[2], h[3]);
+  *reinterpret_cast<uint2 *>(act + (size_t)p * I + i) = o;
+}
+
+// Library-owned fork/join events, created once per device and reused.
+struct StreamEvents {
+  hipEvent_t fork = nullptr, ready = nullptr;
+};
+
+int get_events(StreamEvents *&out) {
+  static StreamEvents ev[64];
+  static int created[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ST_HIP;
+  if (!created[dev]) {
+    if (hipEventCreateWithFlags(&ev[dev].fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ev[dev].ready, hipEventDisableTiming) != hipSuccess)
+      return ST_HIP;
+    created[dev] = 1;
+  }
+  out = &ev[dev];
+  return ST_OK;
+}
+
+constexpr int kTwoStreamMaxT = 256;  // decomposed-path buffers exist up to this many tokens
+
 struct FwdLayout {
-  size_t u_part = 0, act = 0, v_part = 0, total = 0;
+  size_t u_part = 0, act = 0, v_part = 0, g = 0, dlt = 0, total = 0;
   int splits1 = 0, steps1 = 0, splits2 = 0, steps2 = 0, rmax = 0;
+  bool decomposed = false;
 };
 
 FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
@@ -807,6 +858,13 @@ FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
     L.v_part = off;
     off = align256(off + (size_t)L.splits2 * R * L.rmax * sizeof(float));
   }
+  if (has_lora && d.num_tokens <= kTwoStreamMaxT && (d.inter % 4) == 0) {
+    L.decomposed = true;
+    L.g = off;
+    off = align256(off + R * 2 * d.inter * sizeof(float));
+    L.dlt = off;
+    off = align256(off + R * 2 * d.inter * sizeof(float));
+  }
   L.total = off;
   return L;
 }
@@ -822,7 +880,6 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
                    const uint16_t *w2, const moe_lora_adapters *lora, uint16_t *y_perm, void *ws,
                    size_t ws_bytes, hipStream_t main, hipStream_t side,
                    const moe_lora_options *opts) {
-  (void)side;
   const int R = d.num_tokens * d.top_k;
   if (R == 0) return ST_OK;
   const FwdLayout L = layout(d, lora);
@@ -854,37 +911,80 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   const int bm = pick_bm(R, d.num_experts);
   int st;
 
-  // 1) gate_up LoRA shrink: u_part = A1 . x  (split over H)
-  if (has_lora) {
-    GemmParams P = base;
-    P.a = a_src;
-    P.a_gather = a_gather;
-    P.K = d.hidden;
-    P.N = 0;
-    P.k_steps_per_split = L.steps1;
-    for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->a_gate_up[s];
-    P.out_f32 = u_part;
-    if ((st = launch_shrink(P, shrink_bm(R, d.num_experts), L.splits1, main)) != ST_OK) return st;
+  hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->gate_up_event_begin) : nullptr;
+  hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->gate_up_event_end) : nullptr;
+  const int force = opts ? opts->force_path : 0;
+  int two_max = (opts && opts->two_stream_max_tokens > 0) ? opts->two_stream_max_tokens : kTwoStreamMaxT;
+  if (two_max > kTwoStreamMaxT) two_max = kTwoStreamMaxT;
+  const bool decomposed =
+      has_lora && L.decomposed && (force == 2 || (force == 0 && side && d.num_tokens <= two_max));
+  if (force == 2 && has_lora && !L.decomposed) return ST_UNSUPPORTED;
+  // the side stream is used only by the decomposed path
+  hipStream_t lora_stream = (decomposed && side) ? side : main;
+
+  GemmParams shrink1 = base;
+  if (has_lora) {  // gate_up LoRA shrink: u_part = A1 . x  (split over H)
+    shrink1.a = a_src;
+    shrink1.a_gather = a_gather;
+    shrink1.K = d.hidden;
+    shrink1.N = 0;
+    shrink1.k_steps_per_split = L.steps1;
+    for (int s = 0; s < lora->num_slots; ++s) shrink1.lora_w[s] = lora->a_gate_up[s];
+    shrink1.out_f32 = u_part;
   }
-  // 2) gate_up GEMM + LoRA expand + SwiGLU -> act
-  {
-    GemmParams P = base;
-    P.a = a_src;
-    P.a_gather = a_gather;
-    P.w = w1;
-    P.K = d.hidden;
-    P.N = 2 * d.inter;
+  GemmParams gu = base;  // gate_up GEMM
+  gu.a = a_src;
+  gu.a_gather = a_gather;
+  gu.w = w1;
+  gu.K = d.hidden;
+  gu.N = 2 * d.inter;
+
+  if (!decomposed) {
+    // fused: shrink, then the GEMM appends the LoRA expand as extra K steps and applies
+    // SwiGLU in its epilogue
     if (has_lora) {
-      for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->b_gate_up[s];
-      P.part = u_part;
-      P.part_splits = L.splits1;
+      if ((st = launch_shrink(shrink1, shrink_bm(R, d.num_experts), L.splits1, main)) != ST_OK) return st;
+      for (int s = 0; s < lora->num_slots; ++s) gu.lora_w[s] = lora->b_gate_up[s];
+      gu.part = u_part;
+      gu.part_splits = L.splits1;
     }
-    P.out_bf16 = act;
-    hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->gate_up_event_begin) : nullptr;
-    hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->gate_up_event_end) : nullptr;
+    gu.out_bf16 = act;
     if (ev0 && hipEventRecord(ev0, main) != hipSuccess) return ST_HIP;
-    if ((st = launch_gemm<MODE_GATEUP>(P, bm, main)) != ST_OK) return st;
+    if ((st = launch_gemm<MODE_GATEUP>(gu, bm, main)) != ST_OK) return st;
     if (ev1 && hipEventRecord(ev1, main) != hipSuccess) return ST_HIP;
+  } else {
+    // decomposed: the LoRA shrink and expand (delta D) run on the side stream while main
+    // runs the base gate_up GEMM (G); main joins on lora_ready right before the activation,
+    // the delta's only consumer (bf16 PR, two-stream flow).
+    float *Gb = reinterpret_cast<float *>(wsb + L.g);
+    float *Db = reinterpret_cast<float *>(wsb + L.dlt);
+    StreamEvents *sev = nullptr;
+    if (lora_stream != main) {
+      if ((st = get_events(sev)) != ST_OK) return st;
+      if (hipEventRecord(sev->fork, main) != hipSuccess) return ST_HIP;
+      if (hipStreamWaitEvent(lora_stream, sev->fork, 0) != hipSuccess) return ST_HIP;
+    }
+    if ((st = launch_shrink(shrink1, shrink_bm(R, d.num_experts), L.splits1, lora_stream)) != ST_OK)
+      return st;
+    GemmParams ex = base;  // expand: D = s * B1 . bf16(sum u_part), fp32
+    ex.N = 2 * d.inter;
+    ex.K = 0;
+    for (int s = 0; s < lora->num_slots; ++s) ex.lora_w[s] = lora->b_gate_up[s];
+    ex.part = u_part;
+    ex.part_splits = L.splits1;
+    ex.out_f32 = Db;
+    if ((st = launch_gemm<MODE_EXPAND_F32>(ex, bm, lora_stream)) != ST_OK) return st;
+    if (lora_stream != main && hipEventRecord(sev->ready, lora_stream) != hipSuccess) return ST_HIP;
+
+    gu.out_f32 = Gb;
+    if (ev0 && hipEventRecord(ev0, main) != hipSuccess) return ST_HIP;
+    if ((st = launch_gemm<MODE_GATEUP_F32>(gu, bm, main)) != ST_OK) return st;
+    if (ev1 && hipEventRecord(ev1, main) != hipSuccess) return ST_HIP;
+    if (lora_stream != main && hipStreamWaitEvent(main, sev->ready, 0) != hipSuccess) return ST_HIP;
+    const long long nthr = (long long)R * (d.inter / 4);
+    swiglu_join_kernel<<<dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, main>>>(Gb, Db, act, R,
+                                                                                    d.inter);
+    if (hipGetLastError() != hipSuccess) return ST_HIP;
   }
   // 3) down LoRA shrink: v_part = A2 . act  (split over I)
   if (has_lora) {

@@ -93,13 +93,17 @@ class GpuLayer:
     def w_down(self, e):
         return self.w2_np[e] if self.w2_np is not None else self._w2_cached(e)
 
-    @functools.lru_cache(maxsize=None)
     def _w1_cached(self, e):
-        return self.wl.w_gate_up(e)
+        c = self.__dict__.setdefault("_w1c", {})
+        if e not in c:
+            c[e] = self.wl.w_gate_up(e)
+        return c[e]
 
-    @functools.lru_cache(maxsize=None)
     def _w2_cached(self, e):
-        return self.wl.w_down(e)
+        c = self.__dict__.setdefault("_w2c", {})
+        if e not in c:
+            c[e] = self.wl.w_down(e)
+        return c[e]
 
     def oracle_adapters(self):
         ads = []

@@ -260,3 +260,67 @@ def test_empty_batch():
     ml.moe_lora_route(d, g.logits[:0], e, torch.empty((0,), device=dev()), off, e, e, None)
     torch.cuda.synchronize()
     assert (off.cpu() == 0).all()
+
+
+@pytest.mark.timeout(900)
+def test_layer_parity_dsv3_full_weights_sampled():
+    """DeepSeek-V3-style layer at full size (256 experts resident, ~22.5 GB of bf16
+    weights): routing bit-exact on all tokens, outputs on sampled tokens."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    cfg = NAMED_CONFIGS[5]
+    g = gpu_layer(cfg, stream_weights=True)
+    say(f"[layer] {cfg.name}: full weights resident")
+    layer, lora, out = _layer_case(g)
+    rt = layer.last_route(cfg.T, lora)
+    ids, w = g.oracle_route()
+    check_route({"ids": rt.topk_ids.cpu().numpy(), "w": rt.topk_weights.cpu().numpy(),
+                 "off": rt.expert_offsets.cpu().numpy(), "e2p": rt.e2p.cpu().numpy(),
+                 "p2e": rt.p2e.cpu().numpy()}, ids, w, cfg.E)
+    toks = np.array([0, 1, 333, 777, 1000, cfg.T - 1])
+    experts = sorted(set(int(e) for e in ids[toks].reshape(-1)))
+    say(f"  generating {len(experts)} experts' weights for the oracle")
+    with ThreadPoolExecutor(16) as ex:
+        list(ex.map(lambda e: (g.w_gate_up(e), g.w_down(e)), experts))
+    ref = oracle.layer_sampled(g.x_np, ids, w, toks, cfg.I, g.w_gate_up, g.w_down, g.oracle_adapters(),
+                               g.slots_np)
+    assert_layer_close(f64(out)[toks], ref, "dsv3 sampled")
+    _CACHE.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[2], NAMED_CONFIGS[4], RAGGED], ids=lambda c: c.name)
+def test_two_stream_decomposed_path(cfg):
+    """Side-stream LoRA shrink/expand overlapped with the base gate_up GEMM, joined before
+    the activation: within tolerance of the oracle, and bit-identical to the same
+    decomposed pipeline run on one stream."""
+    g = gpu_layer(cfg)
+    say(f"[two-stream] {cfg.name}")
+    layer = g.layer()
+    lora = g.lora_slots()
+    side = torch.cuda.Stream()
+    out_two = layer(g.x, g.logits, lora, side_stream=side).clone()
+    opts = ml.Options()
+    opts.force_path = 2
+    out_one = layer(g.x, g.logits, lora, opts=opts).clone()
+    opts1 = ml.Options()
+    opts1.force_path = 1
+    out_fused = layer(g.x, g.logits, lora, side_stream=side, opts=opts1).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out_two, out_one)
+    ref = _oracle_out(g)
+    assert_layer_close(f64(out_two), ref["out"], f"{cfg.name} two-stream")
+    assert_layer_close(f64(out_fused), ref["out"], f"{cfg.name} fused with side given")
+    # the decomposed buffers exist only for decode-sized batches
+    if cfg.T > 256:
+        pytest.fail("config too large for this test")
+
+
+def test_decomposed_path_rejected_for_large_batches():
+    g = gpu_layer(NAMED_CONFIGS[3])
+    layer = g.layer()
+    opts = ml.Options()
+    opts.force_path = 2
+    with pytest.raises(ml._lib.MoELoRAError) as ei:
+        layer(g.x, g.logits, g.lora_slots(), opts=opts)
+    assert ei.value.status == ml._lib.ERR_UNSUPPORTED
