@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM counter calibration) and exit")
+    ap.add_argument("--only-lora-on", action="store_true",
+                    help="run only the LoRA-on leg (for counter collection)")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -188,6 +190,10 @@ def main():
 
     log("timing LoRA on (gather-on-load)")
     t_on, gate_up_ms = timed(layer, lora, args.steps, args.warmup, gate_up_events=True)
+    if args.only_lora_on:
+        print(json.dumps({"workload": cfg.name, "ms_per_step": round(t_on * 1e3, 4),
+                          "gate_up_us": round(gate_up_ms * 1e3, 2)}), flush=True)
+        return
     log("timing LoRA off (same kernels, no adapters)")
     t_off, gate_up_off_ms = timed(layer, None, args.steps, args.warmup, gate_up_events=True)
     log("timing LoRA on with the explicit permute call")
