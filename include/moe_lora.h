@@ -136,7 +136,8 @@ int moe_lora_version(void);
  *   expanded_to_permuted [T*k] int32, permuted_to_expanded [T*k] int32.
  * Workspace: moe_lora_route_workspace_size(dims) bytes (may be 0 -> ws may be NULL).
  * grouped must be non-NULL for MOE_LORA_ROUTING_DEEPSEEK_V3 and is ignored otherwise.
- * num_tokens above 65536 returns MOE_LORA_ERR_UNSUPPORTED (route in chunks). */
+ * num_tokens above 256 * min(256, 32768 / E) (65536 for E = 128) returns
+ * MOE_LORA_ERR_UNSUPPORTED (route such batches in chunks). */
 size_t moe_lora_route_workspace_size(const moe_lora_dims *dims);
 int moe_lora_route(const moe_lora_dims *dims, int routing, const moe_lora_grouped *grouped,
                    const uint16_t *logits, int32_t *topk_ids, float *topk_weights,

@@ -32,6 +32,7 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kSingleMaxT = 256;    // one workgroup handles the whole batch up to this
 constexpr int kMaxTokPerWg = 256;   // LDS bound of the per-workgroup id buffer
+constexpr int kMaxRouteWg = 256;    // cooperative grid: one workgroup per CU at most
 
 struct RouteParams {
   RouteArgs a;
@@ -92,25 +93,25 @@ MOE_DEV void topk_renormalize(const uint16_t (&v)[EPL], int E, int K, int lane, 
     key[i] = (e < E) ? ((bf16_order_key(v[i]) << 16) | (0xffffu - (uint32_t)e)) : 0u;
   }
   my_e = -1;
-  float my_l = 0.f, l0 = 0.f, sum = 0.f;
+  uint32_t my_key = 0u;
   for (int j = 0; j < K; ++j) {
     uint32_t best = key[0];
 #pragma unroll
     for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
     const uint32_t m = wave_max_u32(best);
-    const int e = (int)(0xffffu - (m & 0xffffu));
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if (key[i] == m) key[i] = 0u;
-    const float l = order_key_to_f32(m >> 16);
-    if (j == 0) l0 = l;
-    sum += expf(l - l0);
-    if (lane == j) {
-      my_e = e;
-      my_l = l;
-    }
+    if (lane == j) my_key = m;
   }
-  my_w = (my_e >= 0) ? expf(my_l - l0) / sum : 0.f;
+  // softmax over the k selected logits (lane j holds the j-th, the largest in lane 0)
+  const float my_l = order_key_to_f32(my_key >> 16);
+  const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_l), 0));
+  const float ex = (lane < K) ? expf(my_l - l0) : 0.f;
+  float sum = 0.f;
+  for (int j = 0; j < K; ++j) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+  if (lane < K) my_e = (int)(0xffffu - (my_key & 0xffffu));
+  my_w = (lane < K) ? ex / sum : 0.f;
 }
 
 // DeepSeek-V3 grouped routing, keys in fp64 (selection); weights in fp32.
@@ -217,20 +218,35 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams P) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) hist_w[i] = 0;
-  __syncthreads();
 
   const int t_begin = blockIdx.x * P.tok_per_wg;
   const int t_end = min(a.T, t_begin + P.tok_per_wg);
+  // this workgroup's logits block [t_begin, t_end) x E, copied with 16-byte loads
+  uint16_t *lg = reinterpret_cast<uint16_t *>(
+      smem + (((size_t)(kRouteWaves * E + P.tok_per_wg * K + 2 * E) * 4 + 15) & ~(size_t)15) +
+      (a.method == MOE_LORA_ROUTING_DEEPSEEK_V3 ? (size_t)kRouteWaves * E * sizeof(double) : 0));
+  {
+    const size_t n = (size_t)(t_end - t_begin) * E;  // elements
+    const uint16_t *src = a.logits + (size_t)t_begin * E;
+    const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
+    if (vec) {
+      for (size_t v = tid; v < n / 8; v += kRouteThreads)
+        reinterpret_cast<u32x4_t *>(lg)[v] = reinterpret_cast<const u32x4_t *>(src)[v];
+      for (size_t i = (n / 8) * 8 + tid; i < n; i += kRouteThreads) lg[i] = src[i];
+    } else {
+      for (size_t i = tid; i < n; i += kRouteThreads) lg[i] = src[i];
+    }
+  }
+  __syncthreads();
   const int tpw = (P.tok_per_wg + kRouteWaves - 1) / kRouteWaves;
   const int w_begin = min(t_end, t_begin + wave * tpw);
   const int w_end = min(t_end, w_begin + tpw);
   const bool dsv3 = a.method == MOE_LORA_ROUTING_DEEPSEEK_V3;
 
   // ---- phase 1: top-k per token
-  uint16_t cur[EPL], nxt[EPL];
-  if (w_begin < w_end) load_row<EPL>(a.logits + (size_t)w_begin * E, E, lane, cur);
+  uint16_t cur[EPL];
   for (int t = w_begin; t < w_end; ++t) {
-    if (t + 1 < w_end) load_row<EPL>(a.logits + (size_t)(t + 1) * E, E, lane, nxt);
+    load_row<EPL>(lg + (size_t)(t - t_begin) * E, E, lane, cur);
     int my_e;
     float my_w;
     if (dsv3)
@@ -244,8 +260,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams P) {
       ids_l[(t - t_begin) * K + lane] = my_e;
       hist_w[wave * E + my_e] += 1;  // the k experts of one token are distinct
     }
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) cur[i] = nxt[i];
   }
   __syncthreads();
 
@@ -258,15 +272,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams P) {
   }
   if (COOP) {
     cg::this_grid().sync();
+    // (expert, workgroup-chunk) pairs spread over all threads, partial sums combined in LDS
     for (int e = tid; e < E; e += kRouteThreads) {
-      int before = 0, total = 0;
-      for (int b = 0; b < P.num_wg; ++b) {
-        const int h = a.hist[(size_t)b * E + e];
-        total += h;
-        before += (b < (int)blockIdx.x) ? h : 0;
+      tot[e] = 0;
+      wgbase[e] = 0;
+    }
+    __syncthreads();
+    const int chunks = (P.num_wg + 15) / 16;
+    for (int q = tid; q < E * chunks; q += kRouteThreads) {
+      const int e = q % E, b0 = (q / E) * 16;
+      int h[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) h[i] = (b0 + i < P.num_wg) ? a.hist[(size_t)(b0 + i) * E + e] : 0;
+      int total = 0, before = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        total += h[i];
+        before += (b0 + i < (int)blockIdx.x) ? h[i] : 0;
       }
-      tot[e] = total;
-      wgbase[e] = before;
+      atomicAdd(&tot[e], total);
+      atomicAdd(&wgbase[e], before);
     }
   } else {
     for (int e = tid; e < E; e += kRouteThreads) wgbase[e] = 0;
@@ -350,6 +375,7 @@ __global__ void zero_offsets_kernel(int32_t *offsets, int n) {
 size_t route_lds_bytes(int E, int K, int tok_per_wg, bool dsv3) {
   size_t b = ((size_t)(kRouteWaves * E + tok_per_wg * K + 2 * E) * 4 + 15) & ~(size_t)15;
   if (dsv3) b += (size_t)kRouteWaves * E * sizeof(double);
+  b += (size_t)tok_per_wg * E * sizeof(uint16_t);  // logits block
   return b;
 }
 
@@ -375,23 +401,44 @@ bool allow_lds(size_t lds) {
   return true;
 }
 
+// tokens per workgroup: bounded by the LDS copy of the logits block (64 KiB) and the id
+// buffer; DeepSeek-V3 tokens are heavier, so they are spread thinner
+int max_tok_per_wg(int E) {
+  const int m = 32768 / E;
+  return m < kMaxTokPerWg ? m : kMaxTokPerWg;
+}
+
+int plan_route(int T, int E, bool dsv3, int &tok_per_wg) {
+  const int mx = max_tok_per_wg(E);
+  if (T <= kSingleMaxT && T <= mx) {
+    tok_per_wg = T;
+    return 1;
+  }
+  int tpw = dsv3 ? 16 : 64;
+  if (tpw > mx) tpw = mx;
+  int n = (T + tpw - 1) / tpw;
+  if (n > kMaxRouteWg) {
+    n = kMaxRouteWg;
+    if ((T + n - 1) / n > mx) return 0;
+  }
+  tok_per_wg = (T + n - 1) / n;
+  return n;
+}
+
 template <int EPL>
 int launch_epl(const RouteArgs &a, hipStream_t s) {
   RouteParams P;
   P.a = a;
   const bool dsv3 = a.method == MOE_LORA_ROUTING_DEEPSEEK_V3;
-  if (a.T <= kSingleMaxT) {
-    P.num_wg = 1;
-    P.tok_per_wg = a.T;
-    const size_t lds = route_lds_bytes(a.E, a.K, P.tok_per_wg, dsv3);
+  const int nwg = plan_route(a.T, a.E, dsv3, P.tok_per_wg);
+  if (nwg <= 0) return ST_UNSUPPORTED;
+  P.num_wg = nwg;
+  const size_t lds = route_lds_bytes(a.E, a.K, P.tok_per_wg, dsv3);
+  if (nwg == 1) {
     if (!allow_lds<EPL, false>(lds)) return ST_HIP;
     route_kernel<EPL, false><<<1, kRouteThreads, lds, s>>>(P);
     return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
   }
-  int nwg = route_num_wg(a.T);
-  P.num_wg = nwg;
-  P.tok_per_wg = (a.T + nwg - 1) / nwg;
-  const size_t lds = route_lds_bytes(a.E, a.K, P.tok_per_wg, dsv3);
   if (!allow_lds<EPL, true>(lds)) return ST_HIP;
   const int lim = max_coresident<EPL>(lds);
   if (lim < nwg) return ST_UNSUPPORTED;
@@ -403,15 +450,14 @@ int launch_epl(const RouteArgs &a, hipStream_t s) {
 
 }  // namespace
 
-int route_num_wg(int T) {
-  if (T <= kSingleMaxT) return 1;
-  int n = (T + 63) / 64;
-  if (n > 128) n = 128;
-  if ((T + n - 1) / n > kMaxTokPerWg) n = (T + kMaxTokPerWg - 1) / kMaxTokPerWg;
-  return n;
+size_t route_workspace_bytes(int T, int E) {
+  // enough for either routing method (DeepSeek-V3 uses the most workgroups)
+  int tpw = 0;
+  const int n = plan_route(T, E, true, tpw);
+  return n > 1 ? (size_t)n * E * sizeof(int32_t) : 0;
 }
 
-int route_max_tokens() { return 256 * kMaxTokPerWg; }
+int route_max_tokens(int E) { return kMaxRouteWg * max_tok_per_wg(E); }
 
 int launch_zero_offsets(int32_t *offsets, int E, hipStream_t s) {
   zero_offsets_kernel<<<1, 256, 0, s>>>(offsets, E + 1);

@@ -44,7 +44,9 @@ def _dims(T=16, H=256, I=128, E=8, k=2):
 def test_workspace_sizes_are_host_only_and_grow_with_lora():
     lib = pkg.load()
     d = _dims()
-    assert lib.moe_lora_route_workspace_size(ctypes.byref(d)) == 1 * 8 * 4
+    assert lib.moe_lora_route_workspace_size(ctypes.byref(d)) == 0  # one workgroup, no grid step
+    big = _lib.Dims(8192, 2048, 768, 128, 8)
+    assert lib.moe_lora_route_workspace_size(ctypes.byref(big)) >= 128 * 128 * 4
     base = lib.moe_lora_forward_workspace_size(ctypes.byref(d), None)
     assert base >= 32 * 128 * 2
     a = _lib.Adapters()
@@ -86,9 +88,15 @@ def test_route_argument_checks():
     assert lib.moe_lora_route(ctypes.byref(d), 1, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                               1 << 20, None) == _lib.ERR_INVALID_ARGUMENT
     g = _lib.Grouped(4, 1, 1.0, None)  # top_k 2 fits one group of 2 experts
-    # workspace too small is reported before launch
-    assert lib.moe_lora_route(ctypes.byref(d), 1, ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              FAKE, 0, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    # workspace too small is reported before launch (a batch large enough for a grid step)
+    dbig = _dims(T=4096)
+    assert lib.moe_lora_route_workspace_size(ctypes.byref(dbig)) > 0
+    assert lib.moe_lora_route(ctypes.byref(dbig), 1, ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, 0, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    # batches beyond the routing kernel's LDS plan are unsupported
+    dhuge = _dims(T=70000)
+    assert lib.moe_lora_route(ctypes.byref(dhuge), 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              1 << 30, None) == _lib.ERR_UNSUPPORTED
     g = _lib.Grouped(4, 1, 1.0, None)
     d3 = _dims(k=3)  # 3 > topk_group * E / n_group = 2
     assert lib.moe_lora_route(ctypes.byref(d3), 1, ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE,
