@@ -121,9 +121,8 @@ const char *moe_lora_status_string(int status);
 int moe_lora_version(void);
 
 /* ---------------------------------------------------------------- route
- * Top-k routing and the expert-sorted pack in one launch (sglang PR "[LoRA]
- * Experimental fast LoRA path ...", Optimizations: top-k and the routed pack in a
- * single launch).
+ * Top-k routing and the expert-sorted pack fused (sglang PR "[LoRA] Experimental fast
+ * LoRA path ...", Optimizations: top-k and the routed pack in a single launch).
  *   Renormalize: top-k of the bf16 logits (ties -> lower expert index), weights =
  *     softmax over the k selected logits.
  *   DeepSeek-V3: s = sigmoid(logit), key = s + correction_bias; groups are contiguous
@@ -135,6 +134,8 @@ int moe_lora_version(void);
  *   expert_offsets [E+1] int32 (exclusive prefix of per-expert counts),
  *   expanded_to_permuted [T*k] int32, permuted_to_expanded [T*k] int32.
  * Workspace: moe_lora_route_workspace_size(dims) bytes (may be 0 -> ws may be NULL).
+ * Batches of up to 256 tokens take one launch; larger ones take two (per-block counts,
+ * then final positions).
  * grouped must be non-NULL for MOE_LORA_ROUTING_DEEPSEEK_V3 and is ignored otherwise.
  * num_tokens above 256 * min(256, 32768 / E) (65536 for E = 128) returns
  * MOE_LORA_ERR_UNSUPPORTED (route such batches in chunks). */

@@ -56,6 +56,10 @@ struct GemmParams {
   int rmax;
   uint16_t *out_bf16;
   float *out_f32;
+  // gate_up only: fused down-LoRA shrink partials v_part[n_tile][p][0:r] = A2[slot][e] . act
+  // over the tile's I columns (NULL = not fused)
+  const uint16_t *down_a[MOE_LORA_MAX_SLOTS];  // [E, r, I]
+  float *down_part;                            // [n_tiles][R][rmax]
 };
 
 template <int BM, int BN, int WM, int WN, int MODE, int PF>
@@ -399,6 +403,14 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
     }
 
     if constexpr (kGateUp) {
+      // SwiGLU in registers; with the fused down shrink the bf16 activation tile also goes
+      // to LDS (pitch HP) so the tile's share of v = A2 . act can be contracted here.
+      constexpr int HC = BN / 2;      // I columns of this tile
+      constexpr int HP = HC + 8;
+      static_assert(BM * HP <= BN * LDSP && 64 * HP <= BN * LDSP, "activation tile must fit LDS");
+      uint16_t *Hs = Bs[0];
+      uint16_t *A2s = Bs[1];
+      const bool fuse_down = P.down_part != nullptr && slot_mask != 0;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -406,14 +418,61 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
-            const int icol = col * (BN / 2) + wn * (WTN / 2) + fh * 16 + (lane & 15);
-            if (r < rows && icol < P.I) {
+            const int c = wn * (WTN / 2) + fh * 16 + (lane & 15);
+            const int icol = col * HC + c;
+            uint32_t hb = 0u;
+            if (icol < P.I) {
               const float g = acc[fm][fh][i];
               const float u = acc[fm][fh + FN / 2][i];
-              const float h = g / (1.0f + expf(-g)) * u;
-              P.out_bf16[(size_t)(row0 + r) * P.I + icol] = (uint16_t)f32_to_bf16(h);
+              hb = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+              if (r < rows) P.out_bf16[(size_t)(row0 + r) * P.I + icol] = (uint16_t)hb;
+            }
+            if (fuse_down) Hs[r * HP + c] = (uint16_t)hb;
+          }
+      if (fuse_down) {
+        constexpr int NF = (BM / 16) * 4;  // (row fragment, rank fragment) pairs, rank <= 64
+        const int icol0 = col * HC;
+        int m = slot_mask;
+        while (m) {
+          const int a = __ffs(m) - 1;
+          m &= m - 1;
+          const int r_a = P.rank[a];
+          const uint16_t *A2 = P.down_a[a] + (size_t)e * r_a * P.I;
+          __syncthreads();  // previous slot's reads of A2s done
+          for (int q = tid; q < 64 * (HC / 8); q += NT) {
+            const int j = q / (HC / 8), c8 = (q % (HC / 8)) * 8;
+            u32x4_t v = zero_u32x4();
+            if (j < r_a && icol0 + c8 < P.I) {
+              const uint16_t *src = A2 + (size_t)j * P.I + icol0 + c8;
+              if ((P.I & 7) == 0) {
+                v = *reinterpret_cast<const u32x4_t *>(src);
+              }
+            }
+            *reinterpret_cast<u32x4_t *>(&A2s[j * HP + c8]) = v;
+          }
+          __syncthreads();  // Hs and A2s visible
+          for (int f = wave; f < NF; f += NT / 64) {
+            const int mf = f / 4, nf = f % 4;
+            if (nf * 16 >= r_a) continue;
+            f32x4_t v4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < HC / 32; ++kk) {
+              const u32x4_t ha = *reinterpret_cast<const u32x4_t *>(
+                  &Hs[(mf * 16 + (lane & 15)) * HP + kk * 32 + (lane >> 4) * 8]);
+              const u32x4_t hb2 = *reinterpret_cast<const u32x4_t *>(
+                  &A2s[(nf * 16 + (lane & 15)) * HP + kk * 32 + (lane >> 4) * 8]);
+              v4 = mfma_16x16x32(ha, hb2, v4);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = mf * 16 + (lane >> 4) * 4 + i;
+              const int j = nf * 16 + (lane & 15);
+              if (r < rows && j < r_a && s_slot[r] == a)
+                P.down_part[((size_t)col * P.R + row0 + r) * P.rmax + j] = v4[i];
             }
           }
+        }
+      }
     } else {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -724,15 +783,19 @@ int pick_bm(int R, int E) {
   return 128;
 }
 
-int shrink_bm(int R, int E) { return (R / (E > 0 ? E : 1)) <= 48 ? 32 : 128; }
+int shrink_bm(int R, int E) {
+  const int avg = R / (E > 0 ? E : 1);
+  return avg <= 16 ? 16 : (avg <= 48 ? 32 : 128);
+}
 
+// split K so that the grid has ~1024 workgroups, each with at least 4 pipelined K steps
 int shrink_splits(int R, int E, int K, int &steps_per_split) {
   const int steps = cdiv(K, BK);
   const int tiles = mtile_bound(R, E, shrink_bm(R, E));
-  int want = cdiv(2048, tiles > 0 ? tiles : 1);
+  int want = cdiv(1024, tiles > 0 ? tiles : 1);
   if (want < 1) want = 1;
-  if (want > steps) want = steps;
   steps_per_split = cdiv(steps, want);
+  if (steps_per_split < 4) steps_per_split = steps < 4 ? steps : 4;
   return cdiv(steps, steps_per_split);
 }
 
@@ -767,6 +830,9 @@ int launch_stream(const GemmParams &P, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
 }
 
+// n-tiles of the gate_up GEMM (each covers BN/2 intermediate columns)
+int gateup_ncols(int bm, int I) { return bm >= 128 ? cdiv(I, 128) : cdiv(I, 64); }
+
 template <int MODE>
 int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
   const int BN = 128;
@@ -775,11 +841,12 @@ int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
     case 16: return launch_cfg<16, 128, 1, 4, MODE, 4>(P, ncols, s);
     case 32: return launch_cfg<32, 128, 1, 4, MODE, 4>(P, ncols, s);
     case 64: return launch_cfg<64, 128, 2, 2, MODE, 2>(P, ncols, s);
-    default: return launch_cfg<128, 256, 2, 4, MODE, 2>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
+    default: return launch_cfg<128, 256, 2, 4, MODE, 4>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
   }
 }
 
 int launch_shrink(const GemmParams &P, int bm, int splits, hipStream_t s) {
+  if (bm <= 16) return launch_cfg<16, 64, 1, 4, MODE_SHRINK, 2>(P, splits, s);
   if (bm <= 32) return launch_cfg<32, 64, 2, 2, MODE_SHRINK, 2>(P, splits, s);
   return launch_cfg<128, 64, 2, 2, MODE_SHRINK, 2>(P, splits, s);
 }
@@ -836,7 +903,7 @@ constexpr int kTwoStreamMaxT = 256;  // decomposed-path buffers exist up to this
 
 struct FwdLayout {
   size_t u_part = 0, act = 0, v_part = 0, g = 0, dlt = 0, total = 0;
-  int splits1 = 0, steps1 = 0, splits2 = 0, steps2 = 0, rmax = 0;
+  int splits1 = 0, steps1 = 0, splits2 = 0, shrink2_splits = 0, steps2 = 0, rmax = 0;
   bool decomposed = false;
 };
 
@@ -848,7 +915,9 @@ FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
   if (has_lora) {
     L.rmax = rmax8(lora);
     L.splits1 = shrink_splits((int)R, d.num_experts, d.hidden, L.steps1);
-    L.splits2 = shrink_splits((int)R, d.num_experts, d.inter, L.steps2);
+    L.shrink2_splits = shrink_splits((int)R, d.num_experts, d.inter, L.steps2);
+    // the fused path writes one down-shrink partial per gate_up n-tile (64 or 128 I columns)
+    L.splits2 = L.shrink2_splits > cdiv(d.inter, 64) ? L.shrink2_splits : cdiv(d.inter, 64);
     L.u_part = off;
     off = align256(off + (size_t)L.splits1 * R * L.rmax * sizeof(float));
   }
@@ -949,6 +1018,10 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       gu.part_splits = L.splits1;
     }
     gu.out_bf16 = act;
+    if (has_lora) {  // the down-LoRA shrink rides in the epilogue (partials per I tile)
+      for (int s = 0; s < lora->num_slots; ++s) gu.down_a[s] = lora->a_down[s];
+      gu.down_part = v_part;
+    }
     if (ev0 && hipEventRecord(ev0, main) != hipSuccess) return ST_HIP;
     if ((st = launch_gemm<MODE_GATEUP>(gu, bm, main)) != ST_OK) return st;
     if (ev1 && hipEventRecord(ev1, main) != hipSuccess) return ST_HIP;
@@ -986,8 +1059,9 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
                                                                                     d.inter);
     if (hipGetLastError() != hipSuccess) return ST_HIP;
   }
-  // 3) down LoRA shrink: v_part = A2 . act  (split over I)
-  if (has_lora) {
+  // 3) down LoRA shrink: v_part = A2 . act  (split over I); fused into the gate_up
+  //    epilogue on the fused path
+  if (has_lora && decomposed) {
     GemmParams P = base;
     P.a = act;
     P.a_gather = 0;
@@ -996,7 +1070,8 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     P.k_steps_per_split = L.steps2;
     for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->a_down[s];
     P.out_f32 = v_part;
-    if ((st = launch_shrink(P, shrink_bm(R, d.num_experts), L.splits2, main)) != ST_OK) return st;
+    if ((st = launch_shrink(P, shrink_bm(R, d.num_experts), L.shrink2_splits, main)) != ST_OK)
+      return st;
   }
   // 4) down GEMM + down LoRA expand -> y_perm (unweighted)
   {
@@ -1009,7 +1084,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     if (has_lora) {
       for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->b_down[s];
       P.part = v_part;
-      P.part_splits = L.splits2;
+      P.part_splits = decomposed ? L.shrink2_splits : gateup_ncols(bm, d.inter);
     }
     P.out_bf16 = y_perm;
     if ((st = launch_gemm<MODE_DOWN>(P, bm, main)) != ST_OK) return st;

@@ -13,17 +13,16 @@
 //   order-preserving 64-bit pattern with a DPP max, and only on a tie of those bits
 //   falls back to the low bits and then to the lower index, so the selection is exact.
 //   Each wave counts its experts in an LDS histogram row of its own.
-// Workgroups then agree on global offsets: a single workgroup (T <= 256) needs no
-//   grid-wide step; larger batches use a cooperative launch with one grid.sync().
+// Batches of up to 256 tokens run in one workgroup and one launch.  Larger batches run on
+//   several workgroups: each writes its per-expert counts and the positions of its rows
+//   relative to its own block; a second, equally wide launch derives the expert offsets
+//   and each block's base and makes the positions final.  (A grid-wide barrier in one
+//   cooperative launch measured ~20 us slower per call than the second launch.)
 // Phase 2: every wave scatters its own contiguous run of expanded rows; the stable
 //   rank among equal experts inside a 64-row chunk comes from ballots over the bits of
 //   the expert id, the base from the per-wave, per-workgroup prefix counts.
-#include <hip/hip_cooperative_groups.h>
-
 #include "common.h"
 #include "kernels.h"
-
-namespace cg = cooperative_groups;
 
 namespace moe {
 namespace {
@@ -32,7 +31,7 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kSingleMaxT = 256;    // one workgroup handles the whole batch up to this
 constexpr int kMaxTokPerWg = 256;   // LDS bound of the per-workgroup id buffer
-constexpr int kMaxRouteWg = 256;    // cooperative grid: one workgroup per CU at most
+constexpr int kMaxRouteWg = 256;    // workgroups of one routing launch
 
 struct RouteParams {
   RouteArgs a;
@@ -193,6 +192,58 @@ MOE_DEV void topk_dsv3(const uint16_t (&v)[EPL], const float *bias, int E, int K
   my_w = (my_e >= 0) ? rsf * my_s / sum : 0.f;
 }
 
+// All-reduce over the 16 lanes of a DPP row (quad swaps, then rotations by 4 and 8).
+MOE_DEV uint32_t row_max_u32(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // xor 1
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // xor 2
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror 4
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror 8
+  return o > v ? o : v;
+}
+
+MOE_DEV float row_sum_f32(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  return v;
+}
+
+// Renormalize for four tokens at once: each 16-lane row of the wavefront owns one token
+// (EPR experts per lane); used when k <= 16.  Row-local DPP reductions need no cross-row
+// traffic, so one instruction stream selects for four tokens.
+template <int EPR>
+MOE_DEV void topk_renormalize_rows(const uint16_t *row_logits, bool valid, int E, int K, int lr,
+                                   int &my_e, float &my_w) {
+  uint32_t key[EPR];
+#pragma unroll
+  for (int i = 0; i < EPR; ++i) {
+    const int e = lr * EPR + i;
+    key[i] = (valid && e < E) ? ((bf16_order_key(row_logits[e]) << 16) | (0xffffu - (uint32_t)e)) : 0u;
+  }
+  uint32_t my_key = 0u, m0 = 0u;
+  for (int j = 0; j < K; ++j) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPR; ++i) best = key[i] > best ? key[i] : best;
+    const uint32_t m = row_max_u32(best);
+#pragma unroll
+    for (int i = 0; i < EPR; ++i)
+      if (key[i] == m) key[i] = 0u;
+    if (j == 0) m0 = m;
+    if (lr == j) my_key = m;
+  }
+  const bool mine = valid && lr < K;
+  const float l0 = order_key_to_f32(m0 >> 16);
+  const float ex = mine ? expf(order_key_to_f32(my_key >> 16) - l0) : 0.f;
+  const float sum = row_sum_f32(ex);
+  my_e = mine ? (int)(0xffffu - (my_key & 0xffffu)) : -1;
+  my_w = mine ? ex / sum : 0.f;
+}
+
 template <int EPL>
 MOE_DEV void load_row(const uint16_t *row, int E, int lane, uint16_t (&v)[EPL]) {
 #pragma unroll
@@ -204,7 +255,7 @@ MOE_DEV void load_row(const uint16_t *row, int E, int lane, uint16_t (&v)[EPL]) 
 
 // Dynamic LDS: hist_w [waves][E] int | ids [tok_per_wg*K] int | tot [E] | wgbase [E]
 //              | keys [waves][E] double (DeepSeek-V3 only)
-template <int EPL, bool COOP>
+template <int EPL, bool MULTI>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams P) {
   const RouteArgs &a = P.a;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -244,8 +295,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams P) {
   const bool dsv3 = a.method == MOE_LORA_ROUTING_DEEPSEEK_V3;
 
   // ---- phase 1: top-k per token
+  if (!dsv3 && K <= 16) {
+    const int rrow = lane >> 4, lr = lane & 15;
+    for (int t0 = w_begin; t0 < w_end; t0 += 4) {
+      const int t = t0 + rrow;
+      const bool tv = t < w_end;
+      int my_e;
+      float my_w;
+      topk_renormalize_rows<4 * EPL>(lg + (size_t)(tv ? t - t_begin : 0) * E, tv, E, K, lr, my_e, my_w);
+      if (my_e >= 0) {
+        a.ids[(size_t)t * K + lr] = my_e;
+        a.weights[(size_t)t * K + lr] = my_w;
+        ids_l[(t - t_begin) * K + lr] = my_e;
+        atomicAdd(&hist_w[wave * E + my_e], 1);
+      }
+    }
+  }
   uint16_t cur[EPL];
-  for (int t = w_begin; t < w_end; ++t) {
+  for (int t = (!dsv3 && K <= 16) ? w_end : w_begin; t < w_end; ++t) {
     load_row<EPL>(lg + (size_t)(t - t_begin) * E, E, lane, cur);
     int my_e;
     float my_w;
@@ -263,42 +330,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams P) {
   }
   __syncthreads();
 
-  // ---- per-expert counts of this workgroup, global totals and this workgroup's base
+  // ---- per-wave starting positions inside this workgroup, workgroup totals
   for (int e = tid; e < E; e += kRouteThreads) {
-    int c = 0;
-    for (int w = 0; w < kRouteWaves; ++w) c += hist_w[w * E + e];
-    tot[e] = c;
-    if (COOP) a.hist[(size_t)blockIdx.x * E + e] = c;
-  }
-  if (COOP) {
-    cg::this_grid().sync();
-    // (expert, workgroup-chunk) pairs spread over all threads, partial sums combined in LDS
-    for (int e = tid; e < E; e += kRouteThreads) {
-      tot[e] = 0;
-      wgbase[e] = 0;
+    int run = 0;
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int c = hist_w[w * E + e];
+      hist_w[w * E + e] = run;
+      run += c;
     }
-    __syncthreads();
-    const int chunks = (P.num_wg + 15) / 16;
-    for (int q = tid; q < E * chunks; q += kRouteThreads) {
-      const int e = q % E, b0 = (q / E) * 16;
-      int h[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) h[i] = (b0 + i < P.num_wg) ? a.hist[(size_t)(b0 + i) * E + e] : 0;
-      int total = 0, before = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        total += h[i];
-        before += (b0 + i < (int)blockIdx.x) ? h[i] : 0;
-      }
-      atomicAdd(&tot[e], total);
-      atomicAdd(&wgbase[e], before);
-    }
-  } else {
-    for (int e = tid; e < E; e += kRouteThreads) wgbase[e] = 0;
+    tot[e] = run;
+    if (MULTI) a.hist[(size_t)blockIdx.x * E + e] = run;
   }
   __syncthreads();
-  if (wave == 0) {
-    // exclusive scan of the totals over experts, consecutive experts per lane
+  if (!MULTI && wave == 0) {
+    // one workgroup: offsets are the exclusive scan of its totals
     const int per_lane = (E + 63) / 64;
     int local = 0;
     for (int q = 0; q < per_lane; ++q) {
@@ -315,27 +360,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams P) {
     for (int q = 0; q < per_lane; ++q) {
       const int e = lane * per_lane + q;
       if (e < E) {
-        const int c = tot[e];
-        if (blockIdx.x == 0) a.offsets[e] = run;
-        wgbase[e] += run;
-        run += c;
+        a.offsets[e] = run;
+        wgbase[e] = run;
+        run += tot[e];
       }
     }
-    if (blockIdx.x == 0 && lane == 63) a.offsets[E] = incl;
+    if (lane == 63) a.offsets[E] = incl;
   }
-  __syncthreads();
-  // per-wave starting positions: offsets + workgroup base + earlier waves of this workgroup
-  for (int e = tid; e < E; e += kRouteThreads) {
-    int run = wgbase[e];
-    for (int w = 0; w < kRouteWaves; ++w) {
-      const int c = hist_w[w * E + e];
-      hist_w[w * E + e] = run;
-      run += c;
-    }
-  }
+  if (MULTI)
+    for (int e = tid; e < E; e += kRouteThreads) wgbase[e] = 0;
   __syncthreads();
 
-  // ---- phase 2: stable scatter of this wave's expanded rows
+  // ---- stable scatter of this wave's expanded rows.  One workgroup writes final
+  // positions; with several, each writes its positions relative to its own block
+  // (into e2p) and the last workgroup to finish adds the global bases.
   int32_t *start = hist_w + wave * E;
   const int j0 = w_begin * K, j1 = w_end * K;
   const int jl0 = t_begin * K;
@@ -347,24 +385,89 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams P) {
     const bool valid = j < j1;
     const int e = valid ? ids_l[j - jl0] : 0;
     uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
+    for (int bb = 0; bb < nbits; ++bb) {
+      const bool bit = (e >> bb) & 1;
       const uint64_t m = __ballot(valid && bit);
       peers &= bit ? m : ~m;
     }
     const int rank = __popcll(peers & lt);
-    int s = 0;
-    if (valid) s = start[e];
+    int sp = 0;
+    if (valid) sp = start[e];
     __builtin_amdgcn_wave_barrier();
     if (valid) {
-      const int pos = s + rank;
+      const int pos = wgbase[e] + sp + rank;
       a.e2p[j] = pos;
-      a.p2e[pos] = j;
-      if ((peers & lt) == 0ull) start[e] = s + __popcll(peers);
+      if (!MULTI) a.p2e[pos] = j;
+      if ((peers & lt) == 0ull) start[e] = sp + __popcll(peers);
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// Second launch for multi-workgroup batches: every workgroup reads all per-workgroup
+// expert counts, derives the expert offsets and its own block's base, and turns the
+// block-relative positions of its rows (left in e2p) into final ones.
+__global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(RouteParams P) {
+  const RouteArgs &a = P.a;
+  const int E = a.E, K = a.K;
+  __shared__ int32_t tot[MOE_LORA_MAX_EXPERTS];
+  __shared__ int32_t base[MOE_LORA_MAX_EXPERTS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kRouteThreads) {
+    tot[e] = 0;
+    base[e] = 0;
+  }
+  __syncthreads();
+  // (expert, 16-workgroup chunk) pairs over all threads
+  const int chunks = (P.num_wg + 15) / 16;
+  for (int q = tid; q < E * chunks; q += kRouteThreads) {
+    const int e = q % E, b0 = (q / E) * 16;
+    int h[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) h[i] = (b0 + i < P.num_wg) ? a.hist[(size_t)(b0 + i) * E + e] : 0;
+    int total = 0, before = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      total += h[i];
+      before += (b0 + i < (int)blockIdx.x) ? h[i] : 0;
+    }
+    atomicAdd(&tot[e], total);
+    atomicAdd(&base[e], before);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int per_lane = (E + 63) / 64;
+    int local = 0;
+    for (int q = 0; q < per_lane; ++q) {
+      const int e = lane * per_lane + q;
+      local += (e < E) ? tot[e] : 0;
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    int run = incl - local;
+    for (int q = 0; q < per_lane; ++q) {
+      const int e = lane * per_lane + q;
+      if (e < E) {
+        if (blockIdx.x == 0) a.offsets[e] = run;
+        base[e] += run;
+        run += tot[e];
+      }
+    }
+    if (blockIdx.x == 0 && lane == 63) a.offsets[E] = incl;
+  }
+  __syncthreads();
+  const int j0 = blockIdx.x * P.tok_per_wg * K;
+  const int j1 = min(a.T, (blockIdx.x + 1) * P.tok_per_wg) * K;
+  for (int j = j0 + tid; j < j1; j += kRouteThreads) {
+    const int pos = base[a.ids[j]] + a.e2p[j];
+    a.e2p[j] = pos;
+    a.p2e[pos] = j;
   }
 }
 
@@ -379,22 +482,11 @@ size_t route_lds_bytes(int E, int K, int tok_per_wg, bool dsv3) {
   return b;
 }
 
-template <int EPL>
-int max_coresident(size_t lds) {
-  int dev = 0, per_cu = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_kernel<EPL, true>, kRouteThreads,
-                                                   lds) != hipSuccess)
-    return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return per_cu * cus;
-}
-
-template <int EPL, bool COOP>
+template <int EPL, bool MULTI>
 bool allow_lds(size_t lds) {
   static size_t granted = 64 * 1024;
   if (lds <= granted) return true;
-  if (hipFuncSetAttribute((const void *)route_kernel<EPL, COOP>,
+  if (hipFuncSetAttribute((const void *)route_kernel<EPL, MULTI>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return false;
   granted = lds;
@@ -440,12 +532,10 @@ int launch_epl(const RouteArgs &a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
   }
   if (!allow_lds<EPL, true>(lds)) return ST_HIP;
-  const int lim = max_coresident<EPL>(lds);
-  if (lim < nwg) return ST_UNSUPPORTED;
-  void *args[] = {&P};
-  hipError_t err = hipLaunchCooperativeKernel((const void *)route_kernel<EPL, true>, dim3(nwg),
-                                              dim3(kRouteThreads), args, (unsigned)lds, s);
-  return err == hipSuccess ? ST_OK : ST_HIP;
+  route_kernel<EPL, true><<<nwg, kRouteThreads, lds, s>>>(P);
+  if (hipGetLastError() != hipSuccess) return ST_HIP;
+  route_finish_kernel<<<nwg, kRouteThreads, 0, s>>>(P);
+  return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
 }
 
 }  // namespace

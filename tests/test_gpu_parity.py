@@ -46,7 +46,7 @@ def run_route(g: GpuLayer, T=None):
                off=torch.empty((c.E + 1,), dtype=torch.int32, device=dev()),
                e2p=torch.empty((R,), dtype=torch.int32, device=dev()),
                p2e=torch.empty((R,), dtype=torch.int32, device=dev()))
-    ws = torch.empty((max(1, ml.moe_lora_route_workspace_size(d)),), dtype=torch.uint8, device=dev())
+    ws = torch.zeros((max(1, ml.moe_lora_route_workspace_size(d)),), dtype=torch.uint8, device=dev())
     ml.moe_lora_route(d, g.logits[:T], out["ids"], out["w"], out["off"], out["e2p"], out["p2e"], ws,
                       g.routing, layer.grouped)
     torch.cuda.synchronize()
@@ -77,7 +77,7 @@ def test_route_parity_named_configs(cfg_id):
              off=torch.empty((cfg.E + 1,), dtype=torch.int32, device=dev()),
              e2p=torch.empty((R,), dtype=torch.int32, device=dev()),
              p2e=torch.empty((R,), dtype=torch.int32, device=dev()))
-    ws = torch.empty((ml.moe_lora_route_workspace_size(d),), dtype=torch.uint8, device=dev())
+    ws = torch.zeros((ml.moe_lora_route_workspace_size(d),), dtype=torch.uint8, device=dev())
     grouped = None
     routing = ml.ROUTING_RENORMALIZE
     bias_t = None
@@ -102,7 +102,7 @@ def _route_case(T, E, k, logits_f32, routing="renormalize", bias=None, n_group=1
              off=torch.empty((E + 1,), dtype=torch.int32, device=dev()),
              e2p=torch.empty((R,), dtype=torch.int32, device=dev()),
              p2e=torch.empty((R,), dtype=torch.int32, device=dev()))
-    ws = torch.empty((ml.moe_lora_route_workspace_size(d),), dtype=torch.uint8, device=dev())
+    ws = torch.zeros((ml.moe_lora_route_workspace_size(d),), dtype=torch.uint8, device=dev())
     grouped, r = None, ml.ROUTING_RENORMALIZE
     if routing == "deepseek_v3":
         r = ml.ROUTING_DEEPSEEK_V3
