@@ -81,6 +81,9 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
   __shared__ int s_src[BM];
   __shared__ int s_slot[BM];
   __shared__ int s_info[4];
+  // LoRA expand A operand of the tile: row r holds bf16(s_a * sum of shrink partials) over
+  // the rank columns of its own slot (zero elsewhere); built once, masked per slot later
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[kHasExt ? BM * LDSP : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -228,59 +231,6 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
     }
   };
 
-  // LoRA expand step for slot a: A = bf16(s_a * sum of partials) on rows of that slot,
-  // B = B_lora[a][e] rows (rank columns), zero beyond the rank.
-  auto load_ext = [&](int a, u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
-    const int ra_rank = P.rank[a];
-    const float sc = P.scaling[a];
-#pragma unroll
-    for (int i = 0; i < A_IT; ++i) {
-      xa[i] = zero_u32x4();
-      const int r = a_row[i];
-      const int j0 = a_c8[i] * 8;
-      if (j0 < ra_rank && s_slot[r] == a) {
-        const int p = row0 + r;
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < P.part_splits; ++sp) {
-          const f32x4_t *srcp =
-              reinterpret_cast<const f32x4_t *>(P.part + ((size_t)sp * P.R + p) * P.rmax + j0);
-          const f32x4_t x0 = srcp[0], x1 = srcp[1];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[q] += x0[q];
-            v[4 + q] += x1[q];
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float lo = (j0 + 2 * q < ra_rank) ? v[2 * q] * sc : 0.f;
-          const float hi = (j0 + 2 * q + 1 < ra_rank) ? v[2 * q + 1] * sc : 0.f;
-          xa[i][q] = pack_bf16x2(lo, hi);
-        }
-      }
-    }
-    const uint16_t *bl = P.lora_w[a];
-#pragma unroll
-    for (int i = 0; i < B_IT; ++i) {
-      xb[i] = zero_u32x4();
-      const int wr = b_wrow[i];
-      const int j0 = b_c8[i] * 8;
-      if (wr >= 0 && j0 < ra_rank) {
-        const uint16_t *srcb = bl + ((size_t)e * P.N + wr) * ra_rank + j0;
-        if ((ra_rank & 7) == 0) {
-          xb[i] = *reinterpret_cast<const u32x4_t *>(srcb);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = (j0 + 2 * q < ra_rank) ? srcb[2 * q] : 0u;
-            const uint32_t hi = (j0 + 2 * q + 1 < ra_rank) ? srcb[2 * q + 1] : 0u;
-            xb[i][q] = lo | (hi << 16);
-          }
-        }
-      }
-    }
-  };
-
   // threads past the chunk count hold a duplicate of another thread's chunk, so every
   // thread stores unconditionally (identical values to the same address)
   auto store_lds = [&](int buf, const u32x4_t(&xa)[A_IT], const u32x4_t(&xb)[B_IT]) {
@@ -306,6 +256,87 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32(af[fm], bfr[fn], acc[fm][fn]);
+    }
+  };
+
+  // B operand of the LoRA expand for slot a: B_lora[a][e] rows (rank columns)
+  auto load_ext_b = [&](int a, u32x4_t(&xb)[B_IT]) {
+    const int ra_rank = P.rank[a];
+    const uint16_t *bl = P.lora_w[a];
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+      xb[i] = zero_u32x4();
+      const int wr = b_wrow[i];
+      const int j0 = b_c8[i] * 8;
+      if (wr >= 0 && j0 < ra_rank) {
+        const uint16_t *srcb = bl + ((size_t)e * P.N + wr) * ra_rank + j0;
+        if ((ra_rank & 7) == 0) {
+          xb[i] = *reinterpret_cast<const u32x4_t *>(srcb);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = (j0 + 2 * q < ra_rank) ? srcb[2 * q] : 0u;
+            const uint32_t hi = (j0 + 2 * q + 1 < ra_rank) ? srcb[2 * q + 1] : 0u;
+            xb[i][q] = lo | (hi << 16);
+          }
+        }
+      }
+    }
+  };
+  auto store_b = [&](int buf, const u32x4_t(&xb)[B_IT]) {
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = xb[i];
+  };
+  // one 64-wide K step of the expand: A rows from Xs masked to the rows of slot a
+  auto compute_ext = [&](int buf, int a) {
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      u32x4_t af[FM], bfr[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = wm * WTM + fm * 16 + (lane & 15);
+        af[fm] = *reinterpret_cast<const u32x4_t *>(&Xs[r * LDSP + kk * 32 + (lane >> 4) * 8]);
+        if (s_slot[r] != a) af[fm] = zero_u32x4();
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        bfr[fn] = *reinterpret_cast<const u32x4_t *>(
+            &Bs[buf][(wn * WTN + fn * 16 + (lane & 15)) * LDSP + kk * 32 + (lane >> 4) * 8]);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32(af[fm], bfr[fn], acc[fm][fn]);
+    }
+  };
+  // Xs: every row's own-slot LoRA input, reduced over the shrink splits once per tile
+  auto build_xs = [&]() {
+    for (int c = tid; c < BM * 8; c += NT) {
+      const int r = c >> 3, j0 = (c & 7) * 8;
+      const int a = s_slot[r];
+      u32x4_t v4 = zero_u32x4();
+      if (a >= 0 && j0 < P.rank[a]) {
+        const int ra_rank = P.rank[a];
+        const float sc = P.scaling[a];
+        const int p = row0 + r;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < P.part_splits; ++sp) {
+          const f32x4_t *srcp =
+              reinterpret_cast<const f32x4_t *>(P.part + ((size_t)sp * P.R + p) * P.rmax + j0);
+          const f32x4_t x0 = srcp[0], x1 = srcp[1];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] += x0[q];
+            v[4 + q] += x1[q];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = (j0 + 2 * q < ra_rank) ? v[2 * q] * sc : 0.f;
+          const float hi = (j0 + 2 * q + 1 < ra_rank) ? v[2 * q + 1] * sc : 0.f;
+          v4[q] = pack_bf16x2(lo, hi);
+        }
+      }
+      *reinterpret_cast<u32x4_t *>(&Xs[r * LDSP + j0]) = v4;
     }
   };
 
@@ -385,6 +416,7 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
   } else {
     const uint16_t *wbase = kHasMain ? P.w + (size_t)e * P.N * P.K : nullptr;
     const int wcount = kGateUp ? 2 * P.I : P.N;
+    if (kHasExt && slot_mask) build_xs();  // visible after the main loop's first barrier
     zero_acc();
     if (kHasMain) {
       const int full = P.K / BK;
@@ -393,12 +425,34 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
         load_tail(full * BK, wbase, wcount, xa, xb);
       });
     }
-    if (kHasExt) {
-      int m = slot_mask;
-      while (m) {
-        const int a = __ffs(m) - 1;
-        m &= m - 1;
-        run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) { load_ext(a, xa, xb); });
+    if (kHasExt && slot_mask) {
+      // B operands of up to PF slots loaded at once into the (now idle) register stages,
+      // then one masked K step per slot with A fragments read from Xs
+      int pending = slot_mask;
+      while (pending) {
+        int batch[PF];
+        int nb = 0;
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          batch[u] = -1;
+          if (pending) {
+            batch[u] = __ffs(pending) - 1;
+            pending &= pending - 1;
+            nb = u + 1;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < PF; ++u)
+          if (batch[u] >= 0) load_ext_b(batch[u], rb[u]);
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          if (batch[u] < 0) continue;
+          store_b(u & 1, rb[u]);
+          __syncthreads();
+          compute_ext(u & 1, batch[u]);
+          __syncthreads();
+        }
+        (void)nb;
       }
     }
 
@@ -430,44 +484,57 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
             if (fuse_down) Hs[r * HP + c] = (uint16_t)hb;
           }
       if (fuse_down) {
-        constexpr int NF = (BM / 16) * 4;  // (row fragment, rank fragment) pairs, rank <= 64
+        // A2 slices of the slots present, packed at 16-row granularity into A2s; as many
+        // slots per batch as fit, one barrier pair per batch
+        constexpr int kCapRows = ((BN * LDSP) / HP) / 16 * 16;
         const int icol0 = col * HC;
-        int m = slot_mask;
-        while (m) {
-          const int a = __ffs(m) - 1;
-          m &= m - 1;
-          const int r_a = P.rank[a];
-          const uint16_t *A2 = P.down_a[a] + (size_t)e * r_a * P.I;
-          __syncthreads();  // previous slot's reads of A2s done
-          for (int q = tid; q < 64 * (HC / 8); q += NT) {
-            const int j = q / (HC / 8), c8 = (q % (HC / 8)) * 8;
-            u32x4_t v = zero_u32x4();
-            if (j < r_a && icol0 + c8 < P.I) {
-              const uint16_t *src = A2 + (size_t)j * P.I + icol0 + c8;
-              if ((P.I & 7) == 0) {
-                v = *reinterpret_cast<const u32x4_t *>(src);
-              }
-            }
-            *reinterpret_cast<u32x4_t *>(&A2s[j * HP + c8]) = v;
+        int pending = slot_mask;
+        while (pending) {
+          int bslot[MOE_LORA_MAX_SLOTS], boff[MOE_LORA_MAX_SLOTS], nbat = 0, rows_used = 0;
+          while (pending) {
+            const int a = __ffs(pending) - 1;
+            const int need = (P.rank[a] + 15) / 16 * 16;
+            if (rows_used + need > kCapRows && nbat > 0) break;
+            bslot[nbat] = a;
+            boff[nbat] = rows_used;
+            rows_used += need;
+            ++nbat;
+            pending &= pending - 1;
           }
-          __syncthreads();  // Hs and A2s visible
-          for (int f = wave; f < NF; f += NT / 64) {
-            const int mf = f / 4, nf = f % 4;
-            if (nf * 16 >= r_a) continue;
+          __syncthreads();  // Hs written / previous batch's reads of A2s done
+          for (int q = tid; q < rows_used * (HC / 8); q += NT) {
+            const int rr = q / (HC / 8), c8 = (q % (HC / 8)) * 8;
+            int bi = 0;
+            while (bi + 1 < nbat && rr >= boff[bi + 1]) ++bi;
+            const int a = bslot[bi], j = rr - boff[bi];
+            u32x4_t v = zero_u32x4();
+            if (j < P.rank[a] && icol0 + c8 < P.I)
+              v = *reinterpret_cast<const u32x4_t *>(P.down_a[a] + ((size_t)e * P.rank[a] + j) * P.I +
+                                                      icol0 + c8);
+            *reinterpret_cast<u32x4_t *>(&A2s[rr * HP + c8]) = v;
+          }
+          __syncthreads();
+          // (row fragment, packed rank fragment) tasks over the waves
+          const int nrf = rows_used / 16;
+          for (int f = wave; f < (BM / 16) * nrf; f += NT / 64) {
+            const int mf = f / nrf, rf = f % nrf;
+            int bi = 0;
+            while (bi + 1 < nbat && rf * 16 >= boff[bi + 1]) ++bi;
+            const int a = bslot[bi];
             f32x4_t v4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < HC / 32; ++kk) {
               const u32x4_t ha = *reinterpret_cast<const u32x4_t *>(
                   &Hs[(mf * 16 + (lane & 15)) * HP + kk * 32 + (lane >> 4) * 8]);
               const u32x4_t hb2 = *reinterpret_cast<const u32x4_t *>(
-                  &A2s[(nf * 16 + (lane & 15)) * HP + kk * 32 + (lane >> 4) * 8]);
+                  &A2s[(rf * 16 + (lane & 15)) * HP + kk * 32 + (lane >> 4) * 8]);
               v4 = mfma_16x16x32(ha, hb2, v4);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = mf * 16 + (lane >> 4) * 4 + i;
-              const int j = nf * 16 + (lane & 15);
-              if (r < rows && j < r_a && s_slot[r] == a)
+              const int j = rf * 16 - boff[bi] + (lane & 15);
+              if (r < rows && j < P.rank[a] && s_slot[r] == a)
                 P.down_part[((size_t)col * P.R + row0 + r) * P.rmax + j] = v4[i];
             }
           }
