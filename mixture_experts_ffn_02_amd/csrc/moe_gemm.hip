@@ -908,7 +908,7 @@ int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
     case 16: return launch_cfg<16, 128, 1, 4, MODE, 4>(P, ncols, s);
     case 32: return launch_cfg<32, 128, 1, 4, MODE, 4>(P, ncols, s);
     case 64: return launch_cfg<64, 128, 2, 2, MODE, 2>(P, ncols, s);
-    default: return launch_cfg<128, 256, 2, 4, MODE, 4>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
+    default: return launch_cfg<128, 256, 4, 2, MODE, 2>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
   }
 }
 
