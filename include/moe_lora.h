@@ -174,7 +174,8 @@ int moe_lora_permute(const moe_lora_dims *dims, const uint16_t *x,
  *           work is ordered before later work on `main`.  NULL = one stream: the fused
  *           path (LoRA expand appended to the GEMM's K loop, SwiGLU in its epilogue).
  *   opts    NULL = defaults.  force_path = 1 forces the fused path, 2 the decomposed path
- *           (on one stream when side is NULL; MOE_LORA_ERR_UNSUPPORTED when T > 256).
+ *           (on one stream when side is NULL; MOE_LORA_ERR_UNSUPPORTED when T > 256); other
+ *           values -> MOE_LORA_ERR_INVALID_ARGUMENT.
  * Workspace: moe_lora_forward_workspace_size(dims, lora) bytes; it includes the
  * decomposed path's fp32 buffers when LoRA is present and T <= 256.
  * Concurrency: the fork/join events are per device and shared by all calls; calls that

@@ -140,6 +140,7 @@ int moe_lora_forward(const moe_lora_dims *d, const uint16_t *x, const uint16_t *
   int st = check_dims(d);
   if (st != MOE_LORA_OK) return st;
   if ((st = check_lora(lora)) != MOE_LORA_OK) return st;
+  if (opts && (opts->force_path < 0 || opts->force_path > 2)) return MOE_LORA_ERR_INVALID_ARGUMENT;
   if (d->num_tokens == 0) return MOE_LORA_OK;
   if (!x && !x_perm) return MOE_LORA_ERR_INVALID_ARGUMENT;
   if ((x && !aligned16(x)) || (x_perm && !aligned16(x_perm))) return MOE_LORA_ERR_INVALID_ARGUMENT;

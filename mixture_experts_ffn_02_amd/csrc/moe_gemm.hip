@@ -25,6 +25,8 @@
 // wavefronts.  Work tiles are (expert, m-tile, n-tile) triples found on the device from
 // expert_offsets; block ids are remapped so each XCD runs a contiguous range of them,
 // keeping an expert's weight and activation tiles in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -34,7 +36,11 @@ namespace {
 enum { MODE_GATEUP = 0, MODE_DOWN = 1, MODE_SHRINK = 2, MODE_GATEUP_F32 = 3, MODE_EXPAND_F32 = 4 };
 
 constexpr int BK = 64;
-constexpr int LDSP = BK + 8;
+// LDS tiles hold rows of BK = 64 bf16 (128 bytes, unpadded) with the row's eight 16-byte
+// chunks XOR-swizzled by (row & 7): the staging stores (8 lanes per row) and the MFMA
+// fragment reads (16 rows per instruction) then both run at full LDS bandwidth on gfx950,
+// where a padded 72-element pitch halves the fragment read rate.
+MOE_DEV int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
 struct GemmParams {
   const uint16_t *a;  // A rows: x [T, K] when a_gather, else [R, K] in permuted order
@@ -62,8 +68,11 @@ struct GemmParams {
   float *down_part;                            // [n_tiles][R][rmax]
 };
 
+// Register budget: decode-height tiles keep three waves per SIMD (the LDS allows three
+// blocks per CU); taller tiles two.
 template <int BM, int BN, int WM, int WN, int MODE, int PF>
-__global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams P) {
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(BM <= 32 ? 3 : 2)))
+void moe_gemm_kernel(const GemmParams P) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -72,18 +81,23 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
   constexpr bool kGateUp = (MODE == MODE_GATEUP);
   constexpr bool kHasMain = (MODE != MODE_EXPAND_F32);
   constexpr bool kHasExt = (MODE == MODE_GATEUP || MODE == MODE_DOWN || MODE == MODE_EXPAND_F32);
+  // Decode-height tiles whose expert has no other m-tile read each weight row exactly once
+  // per launch: those stream it past the caches (non-temporal loads, ~10-15 % more HBM
+  // read bandwidth on MI355X); weights shared by several m-tiles keep normal loads so the
+  // other blocks hit in L2.
+  constexpr bool kStreamB = BM <= 32 && MODE != MODE_SHRINK;
   static_assert(FM >= 1 && FN >= 1, "wave tile too small");
   static_assert(!kGateUp || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
   static_assert(PF >= 2 && PF % 2 == 0, "prefetch depth must be even (two LDS buffers)");
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDSP];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDSP];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
   __shared__ int s_src[BM];
   __shared__ int s_slot[BM];
-  __shared__ int s_info[4];
+  __shared__ int s_info[5];
   // LoRA expand A operand of the tile: row r holds bf16(s_a * sum of shrink partials) over
   // the rank columns of its own slot (zero elsewhere); built once, masked per slot later
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[kHasExt ? BM * LDSP : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[kHasExt ? BM * BK : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -121,15 +135,16 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
           s_info[0] = e;
           s_info[1] = lo + m0;
           s_info[2] = min(BM, cnt - m0);
+          s_info[4] = cnt;
         }
         run += tiles;
       }
     }
   }
   __syncthreads();
-  const int e = s_info[0];
+  const int e = __builtin_amdgcn_readfirstlane(s_info[0]);  // block-uniform values in SGPRs
   if (e < 0) return;
-  const int row0 = s_info[1], rows = s_info[2];
+  const int row0 = __builtin_amdgcn_readfirstlane(s_info[1]), rows = __builtin_amdgcn_readfirstlane(s_info[2]);
 
   const bool need_tok = P.a_gather || P.num_slots > 0;
   for (int r = tid; r < BM; r += NT) {
@@ -148,7 +163,9 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
     if (slot >= 0) atomicOr(&s_info[3], 1 << slot);
   }
   __syncthreads();
-  const int slot_mask = s_info[3];
+  const int slot_mask = __builtin_amdgcn_readfirstlane(s_info[3]);
+  // the expert's rows fit this one tile: its weight rows are read by no other block
+  const bool single_mtile = __builtin_amdgcn_readfirstlane(s_info[4]) <= BM;
 
   // ---- per-thread chunk geometry (fixed for the whole K loop).  Threads without a chunk,
   // padding rows and weight rows past N read a valid row instead (never stored or masked
@@ -165,7 +182,7 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
     a_has[i] = c < A_CH;
     a_row[i] = r;
     a_c8[i] = cc & 7;
-    a_lds[i] = r * LDSP + (cc & 7) * 8;
+    a_lds[i] = lds_off(r, cc & 7);
     const int src = s_src[r] >= 0 ? s_src[r] : src0;
     a_ptr[i] = (kHasMain && src >= 0) ? P.a + (size_t)src * P.K + (cc & 7) * 8 : nullptr;
   }
@@ -178,7 +195,7 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
     const int n = cc >> 3;
     b_has[i] = c < B_CH;
     b_c8[i] = cc & 7;
-    b_lds[i] = n * LDSP + (cc & 7) * 8;
+    b_lds[i] = lds_off(n, cc & 7);
     if (MODE == MODE_SHRINK) {
       b_wrow[i] = n;  // rank row, checked against the slot's rank
     } else if (kGateUp) {
@@ -204,13 +221,17 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
 
   // full 64-wide K step, no predicates (see above)
   auto load_full = [&](int k0, const uint16_t *bbase, int bcount, u32x4_t(&xa)[A_IT],
-                       u32x4_t(&xb)[B_IT]) {
+                       u32x4_t(&xb)[B_IT], auto nt) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) xa[i] = *reinterpret_cast<const u32x4_t *>(a_ptr[i] + k0);
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
       const int wr = (b_wrow[i] >= 0 && b_wrow[i] < bcount) ? b_wrow[i] : 0;
-      xb[i] = *reinterpret_cast<const u32x4_t *>(bbase + (size_t)wr * P.K + k0 + b_c8[i] * 8);
+      const u32x4_t *src = reinterpret_cast<const u32x4_t *>(bbase + (size_t)wr * P.K + k0 + b_c8[i] * 8);
+      if constexpr (decltype(nt)::value)
+        xb[i] = __builtin_nontemporal_load(src);
+      else
+        xb[i] = *src;
     }
   };
   // ragged K tail and padding rows zeroed (used once, off the steady state)
@@ -240,18 +261,22 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
     for (int i = 0; i < B_IT; ++i) *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = xb[i];
   };
 
+  // Fragment rows are 16-aligned bases plus (lane & 15), so the swizzle depends on the lane
+  // alone: one per-lane offset per 32-wide K chunk, everything else folds into immediates.
+  int frag_lane[BK / 32];
+#pragma unroll
+  for (int kk = 0; kk < BK / 32; ++kk) frag_lane[kk] = lds_off(lane & 15, kk * 4 + (lane >> 4));
+
   auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       u32x4_t af[FM], bfr[FN];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
-        af[fm] = *reinterpret_cast<const u32x4_t *>(
-            &As[buf][(wm * WTM + fm * 16 + (lane & 15)) * LDSP + kk * 32 + (lane >> 4) * 8]);
+        af[fm] = *reinterpret_cast<const u32x4_t *>(&As[buf][(wm * WTM + fm * 16) * BK + frag_lane[kk]]);
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        bfr[fn] = *reinterpret_cast<const u32x4_t *>(
-            &Bs[buf][(wn * WTN + fn * 16 + (lane & 15)) * LDSP + kk * 32 + (lane >> 4) * 8]);
+        bfr[fn] = *reinterpret_cast<const u32x4_t *>(&Bs[buf][(wn * WTN + fn * 16) * BK + frag_lane[kk]]);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -295,21 +320,23 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int r = wm * WTM + fm * 16 + (lane & 15);
-        af[fm] = *reinterpret_cast<const u32x4_t *>(&Xs[r * LDSP + kk * 32 + (lane >> 4) * 8]);
+        af[fm] = *reinterpret_cast<const u32x4_t *>(&Xs[(wm * WTM + fm * 16) * BK + frag_lane[kk]]);
         if (s_slot[r] != a) af[fm] = zero_u32x4();
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        bfr[fn] = *reinterpret_cast<const u32x4_t *>(
-            &Bs[buf][(wn * WTN + fn * 16 + (lane & 15)) * LDSP + kk * 32 + (lane >> 4) * 8]);
+        bfr[fn] = *reinterpret_cast<const u32x4_t *>(&Bs[buf][(wn * WTN + fn * 16) * BK + frag_lane[kk]]);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32(af[fm], bfr[fn], acc[fm][fn]);
     }
   };
-  // Xs: every row's own-slot LoRA input, reduced over the shrink splits once per tile
+  // Xs: every row's own-slot LoRA input, reduced over the shrink splits once per tile.
+  // The partials of up to 4 splits are loaded together (one memory latency per group, not
+  // per split) and summed in split order.
   auto build_xs = [&]() {
+    constexpr int G = 4;
     for (int c = tid; c < BM * 8; c += NT) {
       const int r = c >> 3, j0 = (c & 7) * 8;
       const int a = s_slot[r];
@@ -317,17 +344,26 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
       if (a >= 0 && j0 < P.rank[a]) {
         const int ra_rank = P.rank[a];
         const float sc = P.scaling[a];
-        const int p = row0 + r;
+        const f32x4_t *src = reinterpret_cast<const f32x4_t *>(P.part + (size_t)(row0 + r) * P.rmax + j0);
+        const size_t split_stride = (size_t)P.R * P.rmax / 4;  // in f32x4 units
         float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < P.part_splits; ++sp) {
-          const f32x4_t *srcp =
-              reinterpret_cast<const f32x4_t *>(P.part + ((size_t)sp * P.R + p) * P.rmax + j0);
-          const f32x4_t x0 = srcp[0], x1 = srcp[1];
+        for (int sp0 = 0; sp0 < P.part_splits; sp0 += G) {
+          f32x4_t x[G][2];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[q] += x0[q];
-            v[4 + q] += x1[q];
+          for (int q = 0; q < G; ++q) {
+            x[q][0] = x[q][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (sp0 + q < P.part_splits) {
+              x[q][0] = src[(size_t)(sp0 + q) * split_stride];
+              x[q][1] = src[(size_t)(sp0 + q) * split_stride + 1];
+            }
           }
+#pragma unroll
+          for (int q = 0; q < G; ++q)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              v[t] += x[q][0][t];
+              v[4 + t] += x[q][1][t];
+            }
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -336,25 +372,29 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
           v4[q] = pack_bf16x2(lo, hi);
         }
       }
-      *reinterpret_cast<u32x4_t *>(&Xs[r * LDSP + j0]) = v4;
+      *reinterpret_cast<u32x4_t *>(&Xs[lds_off(r, c & 7)]) = v4;
     }
   };
 
   // Full K steps [s_begin, s_end): PF register stages in flight, two LDS buffers, one
   // barrier per step.  The steady-state loop has no branches between a load and the use
-  // of its registers.
-  auto run_full = [&](int s_begin, int s_end, const uint16_t *bbase, int bcount) {
+  // of its registers.  `pre` runs once right after the first loads are issued (so its own
+  // memory latency overlaps theirs); `tail_load(u)` runs at each of the last PF steps
+  // before its compute, when register stage u has been stored and is free again.
+  auto run_full = [&](int s_begin, int s_end, const uint16_t *bbase, int bcount, auto &&pre,
+                      auto &&tail_load, auto nt) {
     const int n = s_end - s_begin;
     const int n_main = (n / PF) * PF;
     if (n_main > 0) {
 #pragma unroll
-      for (int u = 0; u < PF; ++u) load_full((s_begin + u) * BK, bbase, bcount, ra[u], rb[u]);
+      for (int u = 0; u < PF; ++u) load_full((s_begin + u) * BK, bbase, bcount, ra[u], rb[u], nt);
+      pre();
       store_lds(0, ra[0], rb[0]);
       __syncthreads();
       for (int i = 0; i < n_main - PF; i += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-          load_full((s_begin + i + u + PF) * BK, bbase, bcount, ra[u], rb[u]);
+          load_full((s_begin + i + u + PF) * BK, bbase, bcount, ra[u], rb[u], nt);
           compute(u & 1);
           store_lds((u + 1) & 1, ra[(u + 1) % PF], rb[(u + 1) % PF]);
           __syncthreads();
@@ -362,13 +402,16 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
       }
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
+        tail_load(u);
         compute(u & 1);
         if (u + 1 < PF) store_lds((u + 1) & 1, ra[u + 1], rb[u + 1]);
         __syncthreads();
       }
+    } else {
+      pre();
     }
     for (int s = s_begin + n_main; s < s_end; ++s) {
-      load_full(s * BK, bbase, bcount, ra[0], rb[0]);
+      load_full(s * BK, bbase, bcount, ra[0], rb[0], nt);
       store_lds(0, ra[0], rb[0]);
       __syncthreads();
       compute(0);
@@ -395,7 +438,7 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
       const int r_a = P.rank[a];
       const uint16_t *bbase = P.lora_w[a] + (size_t)e * r_a * P.K;
       zero_acc();
-      run_full(s0, s1f, bbase, r_a);
+      run_full(s0, s1f, bbase, r_a, [] {}, [](int) {}, std::false_type{});
       if (s1 > s1f) run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
         load_tail(s1f * BK, bbase, r_a, xa, xb);
       });
@@ -416,34 +459,95 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
   } else {
     const uint16_t *wbase = kHasMain ? P.w + (size_t)e * P.N * P.K : nullptr;
     const int wcount = kGateUp ? 2 * P.I : P.N;
-    if (kHasExt && slot_mask) build_xs();  // visible after the main loop's first barrier
     zero_acc();
+    // The expand's first batch of slots (up to PF, ascending).  When the K loop ends on a
+    // full pipelined step and those ranks are multiples of 8, their B operands are loaded
+    // during the last PF main steps into the register stages those steps free, from
+    // clamped addresses (no predicates), and masked when stored.
+    int batch0[PF];
+    int pending = slot_mask;
+    bool r8 = true;
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      batch0[u] = -1;
+      if (pending) {
+        batch0[u] = __ffs(pending) - 1;
+        pending &= pending - 1;
+        if (P.rank[batch0[u]] & 7) r8 = false;
+      }
+    }
+    const int full = kHasMain ? P.K / BK : 0;
+    // (not on 32-row tiles: their three waves per SIMD leave no registers for it)
+    constexpr bool kExtEarly = kHasExt && kHasMain && BM != 32;
+    const bool ext_early = kExtEarly && slot_mask != 0 && r8 && full >= PF && full % PF == 0 && full * BK == P.K;
+    auto load_ext_b_clamped = [&](int a, u32x4_t(&xb)[B_IT]) {
+      const int ra_rank = P.rank[a];
+      const uint16_t *bl = P.lora_w[a];
+#pragma unroll
+      for (int i = 0; i < B_IT; ++i) {
+        const int wr = b_wrow[i] >= 0 ? b_wrow[i] : 0;
+        const int j0 = b_c8[i] * 8 < ra_rank ? b_c8[i] * 8 : 0;
+        xb[i] = *reinterpret_cast<const u32x4_t *>(bl + ((size_t)e * P.N + wr) * ra_rank + j0);
+      }
+    };
+    auto build = [&] {
+      if (kHasExt && slot_mask) build_xs();  // visible after the main loop's first barrier
+    };
+    auto main_loop = [&](auto nt) {
+      if (kExtEarly && ext_early) {
+        run_full(0, full, wbase, wcount, build, [&](int u) {
+          load_ext_b_clamped(batch0[u] >= 0 ? batch0[u] : batch0[0], rb[u]);
+        }, nt);
+      } else {
+        run_full(0, full, wbase, wcount, build, [](int) {}, nt);
+        if (full * BK < P.K) run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
+          load_tail(full * BK, wbase, wcount, xa, xb);
+        });
+      }
+    };
     if (kHasMain) {
-      const int full = P.K / BK;
-      run_full(0, full, wbase, wcount);
-      if (full * BK < P.K) run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
-        load_tail(full * BK, wbase, wcount, xa, xb);
-      });
+      if constexpr (kStreamB) {
+        if (single_mtile)
+          main_loop(std::true_type{});
+        else
+          main_loop(std::false_type{});
+      } else {
+        main_loop(std::false_type{});
+      }
+    } else {
+      build();
     }
     if (kHasExt && slot_mask) {
       // B operands of up to PF slots loaded at once into the (now idle) register stages,
       // then one masked K step per slot with A fragments read from Xs
-      int pending = slot_mask;
+      pending = slot_mask;
+      bool first = true;
       while (pending) {
         int batch[PF];
-        int nb = 0;
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
           batch[u] = -1;
           if (pending) {
             batch[u] = __ffs(pending) - 1;
             pending &= pending - 1;
-            nb = u + 1;
           }
         }
+        if (first && ext_early) {
+          // already in rb[]: zero the chunks outside B's rows and the slot's rank
 #pragma unroll
-        for (int u = 0; u < PF; ++u)
-          if (batch[u] >= 0) load_ext_b(batch[u], rb[u]);
+          for (int u = 0; u < PF; ++u) {
+            if (batch[u] < 0) continue;
+            const int ra_rank = P.rank[batch[u]];
+#pragma unroll
+            for (int i = 0; i < B_IT; ++i)
+              if (!(b_wrow[i] >= 0 && b_c8[i] * 8 < ra_rank)) rb[u][i] = zero_u32x4();
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < PF; ++u)
+            if (batch[u] >= 0) load_ext_b(batch[u], rb[u]);
+        }
+        first = false;
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
           if (batch[u] < 0) continue;
@@ -452,7 +556,6 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
           compute_ext(u & 1, batch[u]);
           __syncthreads();
         }
-        (void)nb;
       }
     }
 
@@ -461,9 +564,9 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
       // to LDS (pitch HP) so the tile's share of v = A2 . act can be contracted here.
       constexpr int HC = BN / 2;      // I columns of this tile
       constexpr int HP = HC + 8;
-      static_assert(BM * HP <= BN * LDSP && 64 * HP <= BN * LDSP, "activation tile must fit LDS");
-      uint16_t *Hs = Bs[0];
-      uint16_t *A2s = Bs[1];
+      static_assert(BM * HP + 64 * HP <= 2 * BN * BK, "activation tile and one A2 slice must fit LDS");
+      uint16_t *Hs = reinterpret_cast<uint16_t *>(Bs);  // both B buffers are free now: [Hs | A2s]
+      uint16_t *A2s = Hs + BM * HP;
       const bool fuse_down = P.down_part != nullptr && slot_mask != 0;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -486,7 +589,7 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
       if (fuse_down) {
         // A2 slices of the slots present, packed at 16-row granularity into A2s; as many
         // slots per batch as fit, one barrier pair per batch
-        constexpr int kCapRows = ((BN * LDSP) / HP) / 16 * 16;
+        constexpr int kCapRows = ((2 * BN * BK - BM * HP) / HP) / 16 * 16;
         const int icol0 = col * HC;
         int pending = slot_mask;
         while (pending) {
@@ -560,279 +663,7 @@ __global__ __launch_bounds__(WM *WN * 64) void moe_gemm_kernel(const GemmParams 
   }
 }
 
-// ---------------------------------------------------------------- weight-streaming variant
-// Decode-sized tiles (BM <= 32 token rows): every weight element is used by one MFMA
-// row block only, so staging it through LDS buys nothing.  Each wavefront owns 32 weight
-// rows (two 16-row MFMA fragments; for gate_up: 16 gate rows and the 16 matching up rows)
-// and streams them straight from HBM into registers in MFMA operand layout, keeping
-// PF K-steps of loads in flight.  The few token rows are read the same way (they stay in
-// L1/L2, shared by the wavefronts of the block).  No LDS, no barriers: wavefronts run
-// independently, which is what keeps enough bytes in flight to approach HBM bandwidth.
-
-// Per-wave lookup of (expert, first row, rows) for m-tile mt; returns false past the end.
-template <int BM>
-MOE_DEV bool find_tile(const GemmParams &P, int mt, int lane, int &e_out, int &row0, int &rows) {
-  const int per = (P.E + 63) / 64;
-  int local = 0;
-  for (int q = 0; q < per; ++q) {
-    const int e = lane * per + q;
-    if (e < P.E) local += (P.offsets[e + 1] - P.offsets[e] + BM - 1) / BM;
-  }
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  int run = incl - local;
-  int found = -1, f_row0 = 0, f_rows = 0;
-  for (int q = 0; q < per; ++q) {
-    const int e = lane * per + q;
-    if (e < P.E) {
-      const int lo = P.offsets[e], cnt = P.offsets[e + 1] - lo;
-      const int tiles = (cnt + BM - 1) / BM;
-      if (mt >= run && mt < run + tiles) {
-        found = e;
-        f_row0 = lo + (mt - run) * BM;
-        f_rows = min(BM, cnt - (mt - run) * BM);
-      }
-      run += tiles;
-    }
-  }
-  const uint64_t m = __ballot(found >= 0);
-  if (m == 0ull) return false;
-  const int src = __ffsll((unsigned long long)m) - 1;
-  e_out = __builtin_amdgcn_readlane(found, src);
-  row0 = __builtin_amdgcn_readlane(f_row0, src);
-  rows = __builtin_amdgcn_readlane(f_rows, src);
-  return true;
-}
-
-template <int BM, int NW, int MODE>
-__global__ __launch_bounds__(NW * 64) void moe_wstream_kernel(const GemmParams P) {
-  constexpr int FM = BM / 16;
-  constexpr int FN = 2;
-  constexpr int BN = NW * 32;
-  constexpr int PF = 4;
-  constexpr bool kGateUp = (MODE == MODE_GATEUP);
-  static_assert(MODE == MODE_GATEUP || MODE == MODE_DOWN, "streaming variant serves the two GEMMs");
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nb = gridDim.x;
-  const int bid = blockIdx.x;
-  const int L = (bid & 7) * (nb >> 3) + (bid >> 3);
-  const int mt = L / P.n_cols, col = L % P.n_cols;
-  int e, row0, rows;
-  if (!find_tile<BM>(P, mt, lane, e, row0, rows)) return;
-
-  const int lr = lane & 15;       // fragment row / column owned by this lane
-  const int kq = (lane >> 4) * 8; // K offset of this lane inside a 32-wide K slab
-
-  // token rows of this lane (one per 16-row fragment).  Rows past the tile end and weight
-  // rows past N point at a valid row instead (their results are never stored), so the
-  // steady-state loads carry no predicate and the compiler can keep PF steps in flight.
-  const uint16_t *a_ptr[FM];
-  int a_slot[FM];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int r = min(fm * 16 + lr, rows - 1);
-    const int p = row0 + r;
-    const bool need_tok = P.a_gather || P.num_slots > 0;
-    const int tok = need_tok ? P.p2e[p] / P.top_k : 0;
-    a_ptr[fm] = P.a + (size_t)(P.a_gather ? tok : p) * P.K + kq;
-    a_slot[fm] = -1;
-    if (P.num_slots > 0 && fm * 16 + lr < rows) {
-      const int s = P.token_slot[tok];
-      a_slot[fm] = (s >= 0 && s < P.num_slots) ? s : -1;
-    }
-  }
-  // weight rows of this lane (one per fragment)
-  int wrow[FN];
-  const uint16_t *w_ptr[FN];
-#pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    int wr;
-    if (kGateUp) {
-      const int icol = col * (BN / 2) + wave * 16 + lr;
-      wr = (icol < P.I) ? f * P.I + icol : -1;
-    } else {
-      const int n = col * BN + wave * 32 + f * 16 + lr;
-      wr = (n < P.N) ? n : -1;
-    }
-    wrow[f] = wr;
-    w_ptr[f] = P.w + ((size_t)e * P.N + (wr >= 0 ? wr : 0)) * P.K + kq;
-  }
-
-  f32x4_t acc[FM][FN];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int f = 0; f < FN; ++f) acc[fm][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nfull = P.K / 64;  // full 64-wide K steps
-  u32x4_t wa[PF][FM][2], wb[PF][FN][2];
-  auto load_step = [&](int s, u32x4_t (&ra)[FM][2], u32x4_t (&rb)[FN][2]) {
-    const int k0 = s * 64;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        ra[fm][kk] = *reinterpret_cast<const u32x4_t *>(a_ptr[fm] + k0 + kk * 32);
-#pragma unroll
-      for (int f = 0; f < FN; ++f)
-        rb[f][kk] = *reinterpret_cast<const u32x4_t *>(w_ptr[f] + k0 + kk * 32);
-    }
-  };
-  // steady state: PF steps in flight, no branches between the loads and their use
-  const int nmain = (nfull / PF) * PF;
-  if (nmain > 0) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) load_step(u, wa[u], wb[u]);
-    for (int s0 = 0; s0 < nmain - PF; s0 += PF) {
-#pragma unroll
-      for (int u = 0; u < PF; ++u) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int f = 0; f < FN; ++f)
-              acc[fm][f] = mfma_16x16x32(wa[u][fm][kk], wb[u][f][kk], acc[fm][f]);
-        load_step(s0 + u + PF, wa[u], wb[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PF; ++u)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-          for (int f = 0; f < FN; ++f)
-            acc[fm][f] = mfma_16x16x32(wa[u][fm][kk], wb[u][f][kk], acc[fm][f]);
-  }
-  for (int s = nmain; s < nfull; ++s) {  // remaining full steps
-    load_step(s, wa[0], wb[0]);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int f = 0; f < FN; ++f) acc[fm][f] = mfma_16x16x32(wa[0][fm][kk], wb[0][f][kk], acc[fm][f]);
-  }
-  if (nfull * 64 < P.K) {  // ragged K tail: zero the chunks past K
-    const int k0 = nfull * 64;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bool kin = k0 + kk * 32 + kq < P.K;
-      u32x4_t ra[FM], rb[FN];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        ra[fm] = kin ? *reinterpret_cast<const u32x4_t *>(a_ptr[fm] + k0 + kk * 32) : zero_u32x4();
-#pragma unroll
-      for (int f = 0; f < FN; ++f)
-        rb[f] = kin ? *reinterpret_cast<const u32x4_t *>(w_ptr[f] + k0 + kk * 32) : zero_u32x4();
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int f = 0; f < FN; ++f) acc[fm][f] = mfma_16x16x32(ra[fm], rb[f], acc[fm][f]);
-    }
-  }
-
-  // LoRA expand: one 64-wide K step per slot present in the tile
-  if (P.num_slots > 0) {
-    int mask = 0;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-      if (a_slot[fm] >= 0) mask |= 1 << a_slot[fm];
-    mask = __reduce_or_sync(~0ull, mask);
-    while (mask) {
-      const int a = __ffs(mask) - 1;
-      mask &= mask - 1;
-      const int ra_rank = P.rank[a];
-      const float sc = P.scaling[a];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int j0 = kk * 32 + kq;
-        u32x4_t ax[FM], bx[FN];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          ax[fm] = zero_u32x4();
-          if (a_slot[fm] == a && j0 < ra_rank) {
-            const int p = row0 + fm * 16 + lr;
-            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int sp = 0; sp < P.part_splits; ++sp) {
-              const f32x4_t *src =
-                  reinterpret_cast<const f32x4_t *>(P.part + ((size_t)sp * P.R + p) * P.rmax + j0);
-              const f32x4_t x0 = src[0], x1 = src[1];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                v[q] += x0[q];
-                v[4 + q] += x1[q];
-              }
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float lo = (j0 + 2 * q < ra_rank) ? v[2 * q] * sc : 0.f;
-              const float hi = (j0 + 2 * q + 1 < ra_rank) ? v[2 * q + 1] * sc : 0.f;
-              ax[fm][q] = pack_bf16x2(lo, hi);
-            }
-          }
-        }
-        const uint16_t *bl = P.lora_w[a];
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          bx[f] = zero_u32x4();
-          if (wrow[f] >= 0 && j0 < ra_rank) {
-            const uint16_t *src = bl + ((size_t)e * P.N + wrow[f]) * ra_rank + j0;
-            if ((ra_rank & 7) == 0) {
-              bx[f] = *reinterpret_cast<const u32x4_t *>(src);
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const uint32_t lo = (j0 + 2 * q < ra_rank) ? src[2 * q] : 0u;
-                const uint32_t hi = (j0 + 2 * q + 1 < ra_rank) ? src[2 * q + 1] : 0u;
-                bx[f][q] = lo | (hi << 16);
-              }
-            }
-          }
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-          for (int f = 0; f < FN; ++f) acc[fm][f] = mfma_16x16x32(ax[fm], bx[f], acc[fm][f]);
-      }
-    }
-  }
-
-  // epilogue
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = fm * 16 + (lane >> 4) * 4 + i;
-      if (r >= rows) continue;
-      if (kGateUp) {
-        const int icol = col * (BN / 2) + wave * 16 + lr;
-        if (icol < P.I) {
-          const float g = acc[fm][0][i], u = acc[fm][1][i];
-          P.out_bf16[(size_t)(row0 + r) * P.I + icol] = (uint16_t)f32_to_bf16(g / (1.0f + expf(-g)) * u);
-        }
-      } else {
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const int n = col * BN + wave * 32 + f * 16 + lr;
-          if (n < P.N) P.out_bf16[(size_t)(row0 + r) * P.N + n] = (uint16_t)f32_to_bf16(acc[fm][f][i]);
-        }
-      }
-    }
-}
-
 // ---------------------------------------------------------------- host side
-struct TileCfg {
-  int bm;
-};
-
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -881,19 +712,6 @@ int launch_cfg(const GemmParams &P, int n_cols, hipStream_t s) {
   GemmParams Q = P;
   Q.n_cols = n_cols;
   moe_gemm_kernel<BM, BN, WM, WN, MODE, PF><<<dim3((unsigned)blocks), dim3(WM * WN * 64), 0, s>>>(Q);
-  return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
-}
-
-template <int BM, int NW, int MODE>
-int launch_stream(const GemmParams &P, hipStream_t s) {
-  constexpr int BN = NW * 32;
-  const int ncols = (MODE == MODE_GATEUP) ? cdiv(P.I, BN / 2) : cdiv(P.N, BN);
-  int tiles = mtile_bound(P.R, P.E, BM);
-  long long blocks = ((long long)tiles * ncols + 7) & ~7ll;
-  if (blocks == 0) return ST_OK;
-  GemmParams Q = P;
-  Q.n_cols = ncols;
-  moe_wstream_kernel<BM, NW, MODE><<<dim3((unsigned)blocks), dim3(NW * 64), 0, s>>>(Q);
   return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
 }
 

@@ -129,6 +129,14 @@ def test_forward_argument_checks():
     # neither x nor x_perm
     assert lib.moe_lora_forward(ctypes.byref(d), None, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                 1 << 30, None, None, None) == _lib.ERR_INVALID_ARGUMENT
+    # unknown force_path
+    o = _lib.Options()
+    o.force_path = 3
+    assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
+                                None, ctypes.byref(o)) == _lib.ERR_INVALID_ARGUMENT
+    o.force_path = -1
+    assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
+                                None, ctypes.byref(o)) == _lib.ERR_INVALID_ARGUMENT
     a.b_down[0] = None
     assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
                                 None, None) == _lib.ERR_INVALID_ARGUMENT

@@ -316,6 +316,26 @@ def test_two_stream_decomposed_path(cfg):
         pytest.fail("config too large for this test")
 
 
+# a batch whose mean rows per expert selects 64-row tiles, with three adapter slots
+MID = make_config(name="mid_T512_H512_I256_E32_k8", cfg_id=202, T=512, H=512, I=256, E=32, top_k=8,
+                  slots=((32, 1.0), (16, 2.0), (8, 0.5)), slot_assignment="uniform")
+# six adapter slots with uneven ranks up to the maximum
+WIDE = make_config(name="wide_T48_H256_I128_E8_k2_6slots", cfg_id=203, T=48, H=256, I=128, E=8, top_k=2,
+                   slots=((64, 1.0), (48, 0.5), (64, 2.0), (33, 1.0), (64, 0.25), (7, 1.0)),
+                   slot_assignment="uniform")
+
+
+@pytest.mark.parametrize("cfg", [MID, WIDE], ids=lambda c: c.name)
+def test_layer_parity_tile_shapes(cfg):
+    """64-row tiles with three adapter slots, and six slots up to rank 64 (the shrink and
+    expand loops over many slots and uneven ranks)."""
+    g = gpu_layer(cfg)
+    say(f"[layer] {cfg.name}")
+    _, _, out = _layer_case(g)
+    ref = _oracle_out(g)
+    assert_layer_close(f64(out), ref["out"], cfg.name)
+
+
 def test_decomposed_path_rejected_for_large_batches():
     g = gpu_layer(NAMED_CONFIGS[3])
     layer = g.layer()
