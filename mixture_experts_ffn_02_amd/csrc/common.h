@@ -22,6 +22,11 @@ MOE_DEV uint32_t f32_to_bf16(float f) {
 
 MOE_DEV uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
 
+// SwiGLU of one (gate, up) pair: silu(g) * u with silu(g) = g / (1 + e^-g).  Uses the
+// hardware exp2 and reciprocal (a few ulp in fp32, far below the bf16 rounding that
+// follows); e^-g -> inf for very negative g gives g * 0 = -0, the limit of silu.
+MOE_DEV float silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
+
 // 16x16x32 bf16 MFMA: A lane l = row l%16, B lane l = column l%16, both holding the
 // same 8 consecutive K values (group l/16); D lane l holds rows 4*(l/16)+i, column l%16.
 MOE_DEV f32x4_t mfma_16x16x32(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) {

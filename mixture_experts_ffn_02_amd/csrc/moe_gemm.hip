@@ -86,6 +86,7 @@ void moe_gemm_kernel(const GemmParams P) {
   // read bandwidth on MI355X); weights shared by several m-tiles keep normal loads so the
   // other blocks hit in L2.
   constexpr bool kStreamB = BM <= 32 && MODE != MODE_SHRINK;
+  constexpr bool kPersistent = BM >= 64;
   static_assert(FM >= 1 && FN >= 1, "wave tile too small");
   static_assert(!kGateUp || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
   static_assert(PF >= 2 && PF % 2 == 0, "prefetch depth must be even (two LDS buffers)");
@@ -94,7 +95,9 @@ void moe_gemm_kernel(const GemmParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
   __shared__ int s_src[BM];
   __shared__ int s_slot[BM];
-  __shared__ int s_info[5];
+  __shared__ int s_mask[2];  // slots present in the tile, by tile parity
+  __shared__ int s_off[MOE_LORA_MAX_EXPERTS + 1];   // expert_offsets
+  __shared__ int s_tpre[MOE_LORA_MAX_EXPERTS + 1];  // first m-tile index of each expert
   // LoRA expand A operand of the tile: row r holds bf16(s_a * sum of shrink partials) over
   // the rank columns of its own slot (zero elsewhere); built once, masked per slot later
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kHasExt ? BM * BK : 8];
@@ -102,21 +105,17 @@ void moe_gemm_kernel(const GemmParams P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // ---- which (expert, m-tile, column) this block owns
-  const int nb = gridDim.x;
-  const int bid = blockIdx.x;
-  const int L = (bid & 7) * (nb >> 3) + (bid >> 3);
-  const int mt = L / P.n_cols, col = L % P.n_cols;
+  // ---- tile list, once per block: expert offsets and each expert's first m-tile index in
+  // LDS.  Tall tiles (prefill) run persistent blocks that loop over tiles; decode-height
+  // tiles take one tile per block.  The hardware places block b on XCD b % 8.
+  for (int i = tid; i <= P.E; i += NT) s_off[i] = P.offsets[i];
+  __syncthreads();
   if (wave == 0) {
-    if (lane == 0) {
-      s_info[0] = -1;
-      s_info[3] = 0;
-    }
     const int per = (P.E + 63) / 64;
     int local = 0;
     for (int q = 0; q < per; ++q) {
-      const int e = lane * per + q;
-      if (e < P.E) local += (P.offsets[e + 1] - P.offsets[e] + BM - 1) / BM;
+      const int ex = lane * per + q;
+      if (ex < P.E) local += (s_off[ex + 1] - s_off[ex] + BM - 1) / BM;
     }
     int incl = local;
 #pragma unroll
@@ -126,25 +125,49 @@ void moe_gemm_kernel(const GemmParams P) {
     }
     int run = incl - local;
     for (int q = 0; q < per; ++q) {
-      const int e = lane * per + q;
-      if (e < P.E) {
-        const int lo = P.offsets[e], cnt = P.offsets[e + 1] - lo;
-        const int tiles = (cnt + BM - 1) / BM;
-        if (mt >= run && mt < run + tiles) {
-          const int m0 = (mt - run) * BM;
-          s_info[0] = e;
-          s_info[1] = lo + m0;
-          s_info[2] = min(BM, cnt - m0);
-          s_info[4] = cnt;
-        }
-        run += tiles;
+      const int ex = lane * per + q;
+      if (ex < P.E) {
+        s_tpre[ex] = run;
+        run += (s_off[ex + 1] - s_off[ex] + BM - 1) / BM;
       }
     }
+    if (lane == 63) s_tpre[P.E] = incl;
+    if (lane < 2) s_mask[lane] = 0;
   }
   __syncthreads();
-  const int e = __builtin_amdgcn_readfirstlane(s_info[0]);  // block-uniform values in SGPRs
-  if (e < 0) return;
-  const int row0 = __builtin_amdgcn_readfirstlane(s_info[1]), rows = __builtin_amdgcn_readfirstlane(s_info[2]);
+  const int total = __builtin_amdgcn_readfirstlane(s_tpre[P.E]) * P.n_cols;
+
+  // ---- the (m-tile, column) work tiles of this block.  Persistent blocks (a grid of
+  // resident blocks, a multiple of 8): block j of XCD x walks a contiguous share of the
+  // tiles, so the blocks of an XCD work on neighbouring tiles at any moment.  Otherwise
+  // (grid = a bound on the tile count, padded to a multiple of 8) one tile per block,
+  // consecutive tiles on one XCD; the loop below then runs at most once.
+  int L, L_end, L_step;
+  if constexpr (kPersistent) {
+    const int per_xcd = (total + 7) >> 3;
+    L = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    L_end = min(total, (int)(blockIdx.x & 7) * per_xcd + per_xcd);
+    L_step = (int)(gridDim.x >> 3);
+  } else {
+    L = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+    L_end = total;
+    L_step = 0;
+  }
+  int parity = 0;
+  for (; L < L_end; L += L_step, parity ^= 1) {
+  const int mt = L / P.n_cols, col = L % P.n_cols;
+  // expert of m-tile mt: last e with s_tpre[e] <= mt (binary search, same in every lane)
+  int lo_e = 0, hi_e = P.E;  // invariant: s_tpre[lo_e] <= mt < s_tpre[hi_e]
+  while (hi_e - lo_e > 1) {
+    const int mid = (lo_e + hi_e) >> 1;
+    if (s_tpre[mid] <= mt) lo_e = mid;
+    else hi_e = mid;
+  }
+  const int e = __builtin_amdgcn_readfirstlane(lo_e);  // block-uniform values in SGPRs
+  const int cnt = __builtin_amdgcn_readfirstlane(s_off[e + 1] - s_off[e]);
+  const int m0 = (mt - __builtin_amdgcn_readfirstlane(s_tpre[e])) * BM;
+  const int row0 = __builtin_amdgcn_readfirstlane(s_off[e]) + m0;
+  const int rows = min(BM, cnt - m0);
 
   const bool need_tok = P.a_gather || P.num_slots > 0;
   for (int r = tid; r < BM; r += NT) {
@@ -160,12 +183,12 @@ void moe_gemm_kernel(const GemmParams P) {
     }
     s_src[r] = src;
     s_slot[r] = slot;
-    if (slot >= 0) atomicOr(&s_info[3], 1 << slot);
+    if (slot >= 0) atomicOr(&s_mask[parity], 1 << slot);
   }
   __syncthreads();
-  const int slot_mask = __builtin_amdgcn_readfirstlane(s_info[3]);
+  const int slot_mask = __builtin_amdgcn_readfirstlane(s_mask[parity]);
   // the expert's rows fit this one tile: its weight rows are read by no other block
-  const bool single_mtile = __builtin_amdgcn_readfirstlane(s_info[4]) <= BM;
+  const bool single_mtile = cnt <= BM;
 
   // ---- per-thread chunk geometry (fixed for the whole K loop).  Threads without a chunk,
   // padding rows and weight rows past N read a valid row instead (never stored or masked
@@ -455,7 +478,6 @@ void moe_gemm_kernel(const GemmParams P) {
               P.out_f32[((size_t)col * P.R + row0 + r) * P.rmax + n] = acc[fm][fn][i];
           }
     }
-    return;
   } else {
     const uint16_t *wbase = kHasMain ? P.w + (size_t)e * P.N * P.K : nullptr;
     const int wcount = kGateUp ? 2 * P.I : P.N;
@@ -483,11 +505,15 @@ void moe_gemm_kernel(const GemmParams P) {
     auto load_ext_b_clamped = [&](int a, u32x4_t(&xb)[B_IT]) {
       const int ra_rank = P.rank[a];
       const uint16_t *bl = P.lora_w[a];
+      // an opaque copy of e keeps these addresses from being computed before the K loop
+      // (held across it they would spill)
+      int e_late = e;
+      asm volatile("" : "+s"(e_late));
 #pragma unroll
       for (int i = 0; i < B_IT; ++i) {
         const int wr = b_wrow[i] >= 0 ? b_wrow[i] : 0;
         const int j0 = b_c8[i] * 8 < ra_rank ? b_c8[i] * 8 : 0;
-        xb[i] = *reinterpret_cast<const u32x4_t *>(bl + ((size_t)e * P.N + wr) * ra_rank + j0);
+        xb[i] = *reinterpret_cast<const u32x4_t *>(bl + ((size_t)e_late * P.N + wr) * ra_rank + j0);
       }
     };
     auto build = [&] {
@@ -581,7 +607,7 @@ void moe_gemm_kernel(const GemmParams P) {
             if (icol < P.I) {
               const float g = acc[fm][fh][i];
               const float u = acc[fm][fh + FN / 2][i];
-              hb = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+              hb = f32_to_bf16(silu_mul(g, u));
               if (r < rows) P.out_bf16[(size_t)(row0 + r) * P.I + icol] = (uint16_t)hb;
             }
             if (fuse_down) Hs[r * HP + c] = (uint16_t)hb;
@@ -591,25 +617,38 @@ void moe_gemm_kernel(const GemmParams P) {
         // slots per batch as fit, one barrier pair per batch
         constexpr int kCapRows = ((2 * BN * BK - BM * HP) / HP) / 16 * 16;
         const int icol0 = col * HC;
+        // packed row rr of a batch (slot set bmask) -> (slot, rank index); loops over the
+        // slot bits instead of indexing per-batch arrays, which would live in scratch
+        auto locate = [&](int bmask, int rr, int &a, int &j) {
+          a = -1;
+          j = 0;
+          int off = 0;
+          for (int m = bmask; m; m &= m - 1) {
+            const int s = __ffs(m) - 1;
+            const int need = (P.rank[s] + 15) / 16 * 16;
+            if (a < 0 && rr < off + need) {
+              a = s;
+              j = rr - off;
+            }
+            off += need;
+          }
+        };
         int pending = slot_mask;
         while (pending) {
-          int bslot[MOE_LORA_MAX_SLOTS], boff[MOE_LORA_MAX_SLOTS], nbat = 0, rows_used = 0;
+          int bmask = 0, rows_used = 0;
           while (pending) {
             const int a = __ffs(pending) - 1;
             const int need = (P.rank[a] + 15) / 16 * 16;
-            if (rows_used + need > kCapRows && nbat > 0) break;
-            bslot[nbat] = a;
-            boff[nbat] = rows_used;
+            if (rows_used + need > kCapRows && bmask != 0) break;
+            bmask |= 1 << a;
             rows_used += need;
-            ++nbat;
             pending &= pending - 1;
           }
           __syncthreads();  // Hs written / previous batch's reads of A2s done
           for (int q = tid; q < rows_used * (HC / 8); q += NT) {
             const int rr = q / (HC / 8), c8 = (q % (HC / 8)) * 8;
-            int bi = 0;
-            while (bi + 1 < nbat && rr >= boff[bi + 1]) ++bi;
-            const int a = bslot[bi], j = rr - boff[bi];
+            int a, j;
+            locate(bmask, rr, a, j);
             u32x4_t v = zero_u32x4();
             if (j < P.rank[a] && icol0 + c8 < P.I)
               v = *reinterpret_cast<const u32x4_t *>(P.down_a[a] + ((size_t)e * P.rank[a] + j) * P.I +
@@ -621,9 +660,8 @@ void moe_gemm_kernel(const GemmParams P) {
           const int nrf = rows_used / 16;
           for (int f = wave; f < (BM / 16) * nrf; f += NT / 64) {
             const int mf = f / nrf, rf = f % nrf;
-            int bi = 0;
-            while (bi + 1 < nbat && rf * 16 >= boff[bi + 1]) ++bi;
-            const int a = bslot[bi];
+            int a, j16;
+            locate(bmask, rf * 16, a, j16);  // first rank index of this fragment
             f32x4_t v4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < HC / 32; ++kk) {
@@ -636,7 +674,7 @@ void moe_gemm_kernel(const GemmParams P) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = mf * 16 + (lane >> 4) * 4 + i;
-              const int j = rf * 16 - boff[bi] + (lane & 15);
+              const int j = j16 + (lane & 15);
               if (r < rows && j < P.rank[a] && s_slot[r] == a)
                 P.down_part[((size_t)col * P.R + row0 + r) * P.rmax + j] = v4[i];
             }
@@ -661,6 +699,12 @@ void moe_gemm_kernel(const GemmParams P) {
           }
     }
   }
+  // the next tile's slot mask starts empty (its previous reads ended a tile ago); LDS is
+  // reused from here
+  if constexpr (!kPersistent) break;
+  if (tid == 0) s_mask[parity ^ 1] = 0;
+  __syncthreads();
+  }  // tile loop
 }
 
 // ---------------------------------------------------------------- host side
@@ -703,15 +747,40 @@ int rmax8(const moe_lora_adapters *lora) {
   return (r + 7) & ~7;
 }
 
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus[dev] = 0;
+  return cus[dev];
+}
+
 template <int BM, int BN, int WM, int WN, int MODE, int PF>
 int launch_cfg(const GemmParams &P, int n_cols, hipStream_t s) {
+  auto kernel = moe_gemm_kernel<BM, BN, WM, WN, MODE, PF>;
+  constexpr int threads = WM * WN * 64;
   int tiles = mtile_bound(P.R, P.E, BM);
   long long blocks = (long long)tiles * n_cols;
-  blocks = (blocks + 7) & ~7ll;
+  blocks = (blocks + 7) & ~7ll;  // the kernels assume a multiple of 8 (one share per XCD)
   if (blocks == 0) return ST_OK;
+  if (BM >= 64) {  // persistent blocks: as many as can be resident at once
+    static int occ = 0;
+    if (occ == 0) {
+      int o = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, reinterpret_cast<const void *>(kernel), threads, 0) !=
+              hipSuccess || o < 1)
+        o = 1;
+      occ = o;
+    }
+    long long resident = ((long long)device_cus() * occ) & ~7ll;
+    if (resident < 8) resident = 8;
+    if (blocks > resident) blocks = resident;
+  }
   GemmParams Q = P;
   Q.n_cols = n_cols;
-  moe_gemm_kernel<BM, BN, WM, WN, MODE, PF><<<dim3((unsigned)blocks), dim3(WM * WN * 64), 0, s>>>(Q);
+  kernel<<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(Q);
   return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
 }
 
@@ -756,7 +825,7 @@ __global__ __launch_bounds__(256) void swiglu_join_kernel(const float *__restric
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const float gg = g[c] + dg[c], uu = u[c] + du[c];
-    h[c] = gg / (1.0f + expf(-gg)) * uu;
+    h[c] = silu_mul(gg, uu);
   }
   uint2 o;
   o.x = pack_bf16x2(h[0], h[1]);
