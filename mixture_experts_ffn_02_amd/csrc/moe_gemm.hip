@@ -66,6 +66,10 @@ struct GemmParams {
   // over the tile's I columns (NULL = not fused)
   const uint16_t *down_a[MOE_LORA_MAX_SLOTS];  // [E, r, I]
   float *down_part;                            // [n_tiles][R][rmax]
+  // adapter slot of each permuted row (-1 = none): written by the gate_up shrink, read by
+  // the later LoRA kernels instead of token_slot[p2e[p] / k] (one dependent load fewer)
+  int32_t *row_slot_out;
+  const int32_t *row_slot;
 };
 
 // Register budget: decode-height tiles keep three waves per SIMD (the LDS allows three
@@ -169,7 +173,7 @@ void moe_gemm_kernel(const GemmParams P) {
   const int row0 = __builtin_amdgcn_readfirstlane(s_off[e]) + m0;
   const int rows = min(BM, cnt - m0);
 
-  const bool need_tok = P.a_gather || P.num_slots > 0;
+  const bool need_tok = P.a_gather || (P.num_slots > 0 && !P.row_slot);
   for (int r = tid; r < BM; r += NT) {
     int src = -1, slot = -1;
     if (r < rows) {
@@ -177,9 +181,10 @@ void moe_gemm_kernel(const GemmParams P) {
       const int tok = need_tok ? P.p2e[p] / P.top_k : 0;
       src = P.a_gather ? tok : p;
       if (P.num_slots > 0) {
-        const int s = P.token_slot[tok];
+        const int s = P.row_slot ? P.row_slot[p] : P.token_slot[tok];
         slot = (s >= 0 && s < P.num_slots) ? s : -1;
       }
+      if (MODE == MODE_SHRINK && P.row_slot_out && col == 0) P.row_slot_out[p] = slot;
     }
     s_src[r] = src;
     s_slot[r] = slot;
@@ -356,12 +361,19 @@ void moe_gemm_kernel(const GemmParams P) {
     }
   };
   // Xs: every row's own-slot LoRA input, reduced over the shrink splits once per tile.
-  // The partials of up to 4 splits are loaded together (one memory latency per group, not
-  // per split) and summed in split order.
+  // Only the chunks below the widest rank are loaded, one (row, chunk) per thread, with
+  // the partials of up to G splits loaded together (one memory latency per group) and
+  // summed in split order.
   auto build_xs = [&]() {
-    constexpr int G = 4;
-    for (int c = tid; c < BM * 8; c += NT) {
-      const int r = c >> 3, j0 = (c & 7) * 8;
+    constexpr int G = PF >= 4 ? 4 : 8;  // four register stages in flight leave room for 4
+    const int cpr = P.rmax >> 3;  // 8-rank chunks that can hold data (rmax is a multiple of 8)
+    // chunks past rmax are zero
+    for (int c = tid; c < BM * (8 - cpr); c += NT) {
+      const int r = c / (8 - cpr), ch = cpr + c % (8 - cpr);
+      *reinterpret_cast<u32x4_t *>(&Xs[lds_off(r, ch)]) = zero_u32x4();
+    }
+    for (int c = tid; c < BM * cpr; c += NT) {
+      const int r = c / cpr, ch = c % cpr, j0 = ch * 8;
       const int a = s_slot[r];
       u32x4_t v4 = zero_u32x4();
       if (a >= 0 && j0 < P.rank[a]) {
@@ -395,7 +407,7 @@ void moe_gemm_kernel(const GemmParams P) {
           v4[q] = pack_bf16x2(lo, hi);
         }
       }
-      *reinterpret_cast<u32x4_t *>(&Xs[lds_off(r, c & 7)]) = v4;
+      *reinterpret_cast<u32x4_t *>(&Xs[lds_off(r, ch)]) = v4;
     }
   };
 
@@ -856,7 +868,7 @@ int get_events(StreamEvents *&out) {
 constexpr int kTwoStreamMaxT = 256;  // decomposed-path buffers exist up to this many tokens
 
 struct FwdLayout {
-  size_t u_part = 0, act = 0, v_part = 0, g = 0, dlt = 0, total = 0;
+  size_t u_part = 0, act = 0, v_part = 0, g = 0, dlt = 0, row_slot = 0, total = 0;
   int splits1 = 0, steps1 = 0, splits2 = 0, shrink2_splits = 0, steps2 = 0, rmax = 0;
   bool decomposed = false;
 };
@@ -880,6 +892,8 @@ FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
   if (has_lora) {
     L.v_part = off;
     off = align256(off + (size_t)L.splits2 * R * L.rmax * sizeof(float));
+    L.row_slot = off;
+    off = align256(off + R * sizeof(int32_t));
   }
   if (has_lora && d.num_tokens <= kTwoStreamMaxT && (d.inter % 4) == 0) {
     L.decomposed = true;
@@ -912,6 +926,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   uint16_t *act = reinterpret_cast<uint16_t *>(wsb + L.act);
   float *u_part = has_lora ? reinterpret_cast<float *>(wsb + L.u_part) : nullptr;
   float *v_part = has_lora ? reinterpret_cast<float *>(wsb + L.v_part) : nullptr;
+  int32_t *row_slot = has_lora ? reinterpret_cast<int32_t *>(wsb + L.row_slot) : nullptr;
 
   GemmParams base{};
   base.p2e = p2e;
@@ -954,6 +969,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     shrink1.k_steps_per_split = L.steps1;
     for (int s = 0; s < lora->num_slots; ++s) shrink1.lora_w[s] = lora->a_gate_up[s];
     shrink1.out_f32 = u_part;
+    shrink1.row_slot_out = row_slot;
   }
   GemmParams gu = base;  // gate_up GEMM
   gu.a = a_src;
@@ -970,6 +986,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       for (int s = 0; s < lora->num_slots; ++s) gu.lora_w[s] = lora->b_gate_up[s];
       gu.part = u_part;
       gu.part_splits = L.splits1;
+      gu.row_slot = row_slot;
     }
     gu.out_bf16 = act;
     if (has_lora) {  // the down-LoRA shrink rides in the epilogue (partials per I tile)
@@ -999,6 +1016,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     for (int s = 0; s < lora->num_slots; ++s) ex.lora_w[s] = lora->b_gate_up[s];
     ex.part = u_part;
     ex.part_splits = L.splits1;
+    ex.row_slot = row_slot;
     ex.out_f32 = Db;
     if ((st = launch_gemm<MODE_EXPAND_F32>(ex, bm, lora_stream)) != ST_OK) return st;
     if (lora_stream != main && hipEventRecord(sev->ready, lora_stream) != hipSuccess) return ST_HIP;
@@ -1024,6 +1042,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     P.k_steps_per_split = L.steps2;
     for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->a_down[s];
     P.out_f32 = v_part;
+    P.row_slot = row_slot;
     if ((st = launch_shrink(P, shrink_bm(R, d.num_experts), L.shrink2_splits, main)) != ST_OK)
       return st;
   }
@@ -1039,6 +1058,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->b_down[s];
       P.part = v_part;
       P.part_splits = decomposed ? L.shrink2_splits : gateup_ncols(bm, d.inter);
+      P.row_slot = row_slot;
     }
     P.out_bf16 = y_perm;
     if ((st = launch_gemm<MODE_DOWN>(P, bm, main)) != ST_OK) return st;
