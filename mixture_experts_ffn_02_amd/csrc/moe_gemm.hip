@@ -89,7 +89,7 @@ void moe_gemm_kernel(const GemmParams P) {
   // per launch: those stream it past the caches (non-temporal loads, ~10-15 % more HBM
   // read bandwidth on MI355X); weights shared by several m-tiles keep normal loads so the
   // other blocks hit in L2.
-  constexpr bool kStreamB = BM <= 32 && MODE != MODE_SHRINK;
+  constexpr bool kStreamB = BM <= 64 && MODE != MODE_SHRINK;
   constexpr bool kPersistent = BM >= 64;
   static_assert(FM >= 1 && FN >= 1, "wave tile too small");
   static_assert(!kGateUp || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
@@ -511,8 +511,7 @@ void moe_gemm_kernel(const GemmParams P) {
       }
     }
     const int full = kHasMain ? P.K / BK : 0;
-    // (not on 32-row tiles: their three waves per SIMD leave no registers for it)
-    constexpr bool kExtEarly = kHasExt && kHasMain && BM != 32;
+    constexpr bool kExtEarly = kHasExt && kHasMain;
     const bool ext_early = kExtEarly && slot_mask != 0 && r8 && full >= PF && full % PF == 0 && full * BK == P.K;
     auto load_ext_b_clamped = [&](int a, u32x4_t(&xb)[B_IT]) {
       const int ra_rank = P.rank[a];
@@ -728,11 +727,13 @@ int mtile_bound(int R, int E, int BM) {
   return (int)((R + nonempty * (BM - 1) + BM - 1) / BM);
 }
 
-// tile height from the mean rows per expert (the routed load is only known on device)
+// Tile height from the mean rows per expert (the routed load is only known on device).
+// Above 16 rows the 64-row tile keeps most experts in one m-tile, so each weight row is
+// streamed from HBM once (a 32-row tile re-read the weights of every expert with more
+// than 32 rows: 1.7x slower on a DeepSeek-V3-sized layer).
 int pick_bm(int R, int E) {
   const int avg = R / (E > 0 ? E : 1);
   if (avg <= 16) return 16;
-  if (avg <= 48) return 32;
   if (avg <= 128) return 64;
   return 128;
 }
@@ -805,7 +806,6 @@ int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
   const int ncols = (MODE == MODE_GATEUP) ? cdiv(P.I, BN / 2) : cdiv(P.N, BN);
   switch (bm) {
     case 16: return launch_cfg<16, 128, 1, 4, MODE, 4>(P, ncols, s);
-    case 32: return launch_cfg<32, 128, 1, 4, MODE, 4>(P, ncols, s);
     case 64: return launch_cfg<64, 128, 2, 2, MODE, 2>(P, ncols, s);
     default: return launch_cfg<128, 256, 4, 2, MODE, 2>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
   }
