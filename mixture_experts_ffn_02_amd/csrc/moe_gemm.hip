@@ -728,12 +728,12 @@ int mtile_bound(int R, int E, int BM) {
 }
 
 // Tile height from the mean rows per expert (the routed load is only known on device).
-// Above 16 rows the 64-row tile keeps most experts in one m-tile, so each weight row is
-// streamed from HBM once (a 32-row tile re-read the weights of every expert with more
-// than 32 rows: 1.7x slower on a DeepSeek-V3-sized layer).
+// Above 8 rows the 64-row tile keeps most experts in one m-tile, so each weight row is
+// streamed from HBM once (tiles of 16 or 32 rows re-read the weights of every expert
+// with more rows: 1.2x slower at 16 rows per expert, 1.7x on a DeepSeek-V3-sized layer).
 int pick_bm(int R, int E) {
   const int avg = R / (E > 0 ? E : 1);
-  if (avg <= 16) return 16;
+  if (avg <= 8) return 16;
   if (avg <= 128) return 64;
   return 128;
 }
