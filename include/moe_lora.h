@@ -134,7 +134,7 @@ int moe_lora_version(void);
  *   expert_offsets [E+1] int32 (exclusive prefix of per-expert counts),
  *   expanded_to_permuted [T*k] int32, permuted_to_expanded [T*k] int32.
  * Workspace: moe_lora_route_workspace_size(dims) bytes (may be 0 -> ws may be NULL).
- * Batches of up to 256 tokens take one launch; larger ones take two (per-block counts,
+ * Batches of up to 64 tokens take one launch; larger ones take two (per-block counts,
  * then final positions).
  * grouped must be non-NULL for MOE_LORA_ROUTING_DEEPSEEK_V3 and is ignored otherwise.
  * num_tokens above 256 * min(256, 32768 / E) (65536 for E = 128) returns
