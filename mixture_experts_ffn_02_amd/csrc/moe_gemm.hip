@@ -50,8 +50,9 @@ struct GemmParams {
   int N, K, I;
   const int32_t *offsets;
   int E, top_k, R;
-  int n_cols;  // n-tiles (GEMM modes) or K splits (SHRINK)
+  int n_cols;  // n-tiles (GEMM modes) or K splits x slot groups (SHRINK)
   int k_steps_per_split;
+  int slot_groups;  // SHRINK: blocks per (m-tile, K split); group g takes slots g, g + groups, ...
   int num_slots;
   const int32_t *token_slot;
   int rank[MOE_LORA_MAX_SLOTS];
@@ -465,10 +466,12 @@ void moe_gemm_kernel(const GemmParams P) {
   if constexpr (MODE == MODE_SHRINK) {
     const int steps_total = (P.K + BK - 1) / BK;
     const int full_total = P.K / BK;
-    const int s0 = col * P.k_steps_per_split;
+    const int groups = P.slot_groups > 1 ? P.slot_groups : 1;
+    const int split = col / groups;
+    const int s0 = split * P.k_steps_per_split;
     const int s1 = min(steps_total, s0 + P.k_steps_per_split);
     const int s1f = min(s1, full_total);
-    for (int a = 0; a < P.num_slots; ++a) {
+    for (int a = col % groups; a < P.num_slots; a += groups) {
       if (!((slot_mask >> a) & 1)) continue;
       const int r_a = P.rank[a];
       const uint16_t *bbase = P.lora_w[a] + (size_t)e * r_a * P.K;
@@ -487,7 +490,7 @@ void moe_gemm_kernel(const GemmParams P) {
             const int r = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
             const int n = wn * WTN + fn * 16 + (lane & 15);
             if (r < rows && n < r_a && s_slot[r] == a)
-              P.out_f32[((size_t)col * P.R + row0 + r) * P.rmax + n] = acc[fm][fn][i];
+              P.out_f32[((size_t)split * P.R + row0 + r) * P.rmax + n] = acc[fm][fn][i];
           }
     }
   } else {
@@ -597,8 +600,10 @@ void moe_gemm_kernel(const GemmParams P) {
     }
 
     if constexpr (kGateUp) {
-      // SwiGLU in registers; with the fused down shrink the bf16 activation tile also goes
-      // to LDS (pitch HP) so the tile's share of v = A2 . act can be contracted here.
+      // SwiGLU in registers; the bf16 activation tile goes to LDS (pitch HP), from where it
+      // is written out in 16-byte row chunks (the fragment layout would give 2-byte
+      // stores) and, with the fused down shrink, contracted with A2 for the tile's share
+      // of v = A2 . act.
       constexpr int HC = BN / 2;      // I columns of this tile
       constexpr int HP = HC + 8;
       static_assert(BM * HP + 64 * HP <= 2 * BN * BK, "activation tile and one A2 slice must fit LDS");
@@ -613,16 +618,18 @@ void moe_gemm_kernel(const GemmParams P) {
           for (int i = 0; i < 4; ++i) {
             const int r = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
             const int c = wn * (WTN / 2) + fh * 16 + (lane & 15);
-            const int icol = col * HC + c;
-            uint32_t hb = 0u;
-            if (icol < P.I) {
-              const float g = acc[fm][fh][i];
-              const float u = acc[fm][fh + FN / 2][i];
-              hb = f32_to_bf16(silu_mul(g, u));
-              if (r < rows) P.out_bf16[(size_t)(row0 + r) * P.I + icol] = (uint16_t)hb;
-            }
-            if (fuse_down) Hs[r * HP + c] = (uint16_t)hb;
+            const float g = acc[fm][fh][i];
+            const float u = acc[fm][fh + FN / 2][i];
+            Hs[r * HP + c] = (uint16_t)f32_to_bf16(silu_mul(g, u));
           }
+      __syncthreads();
+      for (int q = tid; q < BM * (HC / 8); q += NT) {
+        const int r = q / (HC / 8), c8 = (q % (HC / 8)) * 8;
+        const int icol = col * HC + c8;  // I is a multiple of 8: a chunk is all in or all out
+        if (r < rows && icol < P.I)
+          *reinterpret_cast<u32x4_t *>(P.out_bf16 + (size_t)(row0 + r) * P.I + icol) =
+              *reinterpret_cast<const u32x4_t *>(&Hs[r * HP + c8]);
+      }
       if (fuse_down) {
         // A2 slices of the slots present, packed at 16-row granularity into A2s; as many
         // slots per batch as fit, one barrier pair per batch
@@ -692,6 +699,37 @@ void moe_gemm_kernel(const GemmParams P) {
           }
         }
       }
+    } else if constexpr (MODE == MODE_DOWN) {
+      // bf16 output tile through LDS (pitch OP) for 16-byte row-chunk stores; a tile whose
+      // rows do not fit the B buffers at once goes in two row halves
+      constexpr int OP = BN + 8;
+      constexpr int RH = (BM * OP <= 2 * BN * BK) ? BM : BM / 2;
+      static_assert(RH * OP <= 2 * BN * BK && RH % WTM == 0, "output rows must fit the B buffers");
+      uint16_t *Os = reinterpret_cast<uint16_t *>(Bs);
+#pragma unroll
+      for (int h = 0; h < BM / RH; ++h) {
+        if (h) __syncthreads();  // the previous half has been read
+        if ((wm * WTM) / RH == h) {
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = wm * WTM - h * RH + fm * 16 + (lane >> 4) * 4 + i;
+                const int c = wn * WTN + fn * 16 + (lane & 15);
+                Os[r * OP + c] = (uint16_t)f32_to_bf16(acc[fm][fn][i]);
+              }
+        }
+        __syncthreads();
+        for (int q = tid; q < RH * (BN / 8); q += NT) {
+          const int r = q / (BN / 8), c8 = (q % (BN / 8)) * 8;
+          const int n = col * BN + c8;  // N is a multiple of 8: a chunk is all in or all out
+          if (h * RH + r < rows && n < P.N)
+            *reinterpret_cast<u32x4_t *>(P.out_bf16 + (size_t)(row0 + h * RH + r) * P.N + n) =
+                *reinterpret_cast<const u32x4_t *>(&Os[r * OP + c8]);
+        }
+      }
     } else {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -701,12 +739,7 @@ void moe_gemm_kernel(const GemmParams P) {
           for (int i = 0; i < 4; ++i) {
             const int r = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
             const int n = col * BN + wn * WTN + fn * 16 + (lane & 15);
-            if (r < rows && n < P.N) {
-              if constexpr (MODE == MODE_DOWN)
-                P.out_bf16[(size_t)(row0 + r) * P.N + n] = (uint16_t)f32_to_bf16(acc[fm][fn][i]);
-              else
-                P.out_f32[(size_t)(row0 + r) * P.N + n] = acc[fm][fn][i];
-            }
+            if (r < rows && n < P.N) P.out_f32[(size_t)(row0 + r) * P.N + n] = acc[fm][fn][i];
           }
     }
   }
@@ -743,10 +776,12 @@ int shrink_bm(int R, int E) {
   return avg <= 16 ? 16 : (avg <= 48 ? 32 : 128);
 }
 
-// split K so that the grid has ~1024 workgroups, each with at least 4 pipelined K steps
-int shrink_splits(int R, int E, int K, int &steps_per_split) {
+// Split K so that the grid has ~1024 workgroups, each with at least 4 pipelined K steps.
+// With several adapter slots each (m-tile, split) gets one block per slot (slot groups),
+// so the slots' passes over K run side by side instead of one after another in a block.
+int shrink_splits(int R, int E, int K, int groups, int &steps_per_split) {
   const int steps = cdiv(K, BK);
-  const int tiles = mtile_bound(R, E, shrink_bm(R, E));
+  const int tiles = mtile_bound(R, E, shrink_bm(R, E)) * (groups > 1 ? groups : 1);
   int want = cdiv(1024, tiles > 0 ? tiles : 1);
   if (want < 1) want = 1;
   steps_per_split = cdiv(steps, want);
@@ -811,10 +846,13 @@ int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
   }
 }
 
-int launch_shrink(const GemmParams &P, int bm, int splits, hipStream_t s) {
-  if (bm <= 16) return launch_cfg<16, 64, 1, 4, MODE_SHRINK, 2>(P, splits, s);
-  if (bm <= 32) return launch_cfg<32, 64, 2, 2, MODE_SHRINK, 2>(P, splits, s);
-  return launch_cfg<128, 64, 2, 2, MODE_SHRINK, 2>(P, splits, s);
+int launch_shrink(const GemmParams &P0, int bm, int splits, hipStream_t s) {
+  GemmParams P = P0;
+  P.slot_groups = P.num_slots > 1 ? P.num_slots : 1;
+  const int cols = splits * P.slot_groups;
+  if (bm <= 16) return launch_cfg<16, 64, 1, 4, MODE_SHRINK, 2>(P, cols, s);
+  if (bm <= 32) return launch_cfg<32, 64, 2, 2, MODE_SHRINK, 2>(P, cols, s);
+  return launch_cfg<128, 64, 2, 2, MODE_SHRINK, 2>(P, cols, s);
 }
 
 // Activation of the decomposed path: act = silu(G_gate + D_gate) * (G_up + D_up), the
@@ -880,8 +918,8 @@ FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
   size_t off = 0;
   if (has_lora) {
     L.rmax = rmax8(lora);
-    L.splits1 = shrink_splits((int)R, d.num_experts, d.hidden, L.steps1);
-    L.shrink2_splits = shrink_splits((int)R, d.num_experts, d.inter, L.steps2);
+    L.splits1 = shrink_splits((int)R, d.num_experts, d.hidden, lora->num_slots, L.steps1);
+    L.shrink2_splits = shrink_splits((int)R, d.num_experts, d.inter, lora->num_slots, L.steps2);
     // the fused path writes one down-shrink partial per gate_up n-tile (64 or 128 I columns)
     L.splits2 = L.shrink2_splits > cdiv(d.inter, 64) ? L.shrink2_splits : cdiv(d.inter, 64);
     L.u_part = off;
