@@ -42,6 +42,28 @@ constexpr int BK = 64;
 // where a padded 72-element pitch halves the fragment read rate.
 MOE_DEV int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
+// One 16-byte chunk per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane l of the wave writes LDS bytes [base + 16 l, base + 16 l + 16).
+// No registers hold the data and nothing waits for it here; like any vector load it counts
+// in vmcnt, so a later wait for a younger load also covers it.  M0 carries the wave's LDS
+// base and is restored afterwards.
+MOE_DEV void lds_dma16(const void *src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+
+MOE_DEV uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
 struct GemmParams {
   const uint16_t *a;  // A rows: x [T, K] when a_gather, else [R, K] in permuted order
   const int32_t *p2e;
@@ -106,6 +128,16 @@ void moe_gemm_kernel(const GemmParams P) {
   // LoRA expand A operand of the tile: row r holds bf16(s_a * sum of shrink partials) over
   // the rank columns of its own slot (zero elsewhere); built once, masked per slot later
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kHasExt ? BM * BK : 8];
+  // gate_up with the fused down shrink on tiles of 64 rows or more: the tile's A2 slices,
+  // copied into LDS when the tile starts so that their latency overlaps the K loop instead
+  // of the epilogue (rows of all slots packed at 16-row granularity, HC elements per row
+  // with the 16-byte chunks XOR-swizzled by row).  Decode-height tiles keep the LDS and
+  // registers this would take (other blocks on the CU hide their epilogue).
+  constexpr int HC = BN / 2, HP = HC + 8;
+  constexpr bool kA2Pre = kGateUp && BM >= 64;
+  constexpr int kA2Rows = 128;
+  static_assert((kA2Rows * HC / 8) % 64 == 0, "A2 region must be whole wave copies");
+  __shared__ __attribute__((aligned(16))) uint16_t A2p[kA2Pre ? kA2Rows * HC : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -530,7 +562,62 @@ void moe_gemm_kernel(const GemmParams P) {
         xb[i] = *reinterpret_cast<const u32x4_t *>(bl + ((size_t)e_late * P.N + wr) * ra_rank + j0);
       }
     };
+    // packed row rr of the slot set bmask -> (slot, rank index); loops over the slot bits
+    // instead of indexing per-batch arrays, which would live in scratch
+    auto locate = [&](int bmask, int rr, int &a, int &j) {
+      a = -1;
+      j = 0;
+      int off = 0;
+      for (int m = bmask; m; m &= m - 1) {
+        const int s = __ffs(m) - 1;
+        const int need = (P.rank[s] + 15) / 16 * 16;
+        if (a < 0 && rr < off + need) {
+          a = s;
+          j = rr - off;
+        }
+        off += need;
+      }
+    };
+    int a2_rows = 0;
+    for (int m = slot_mask; m; m &= m - 1) a2_rows += (P.rank[__ffs(m) - 1] + 15) / 16 * 16;
+    const bool a2_pre = kA2Pre && P.down_part != nullptr && slot_mask != 0 && a2_rows <= kA2Rows;
+    // A2 rows of every slot in the tile straight into LDS, issued right after the first K
+    // steps' loads; nothing waits for them before the epilogue (chunk q of the region is row q / (HC / 8), physical chunk q % (HC / 8); rows past a
+    // slot's rank and columns past I read a valid element and are never used)
+    auto a2_copy = [&] {
+      if constexpr (kA2Pre) {
+        if (!a2_pre) return;
+        const int icol0 = col * HC;
+        const int copies = (a2_rows * (HC / 8) + 63) / 64;
+        const uint32_t base = lds_addr(A2p);
+        for (int t = wave; t < copies; t += NT / 64) {
+          const int q = t * 64 + lane;
+          const int rr = q / (HC / 8) < a2_rows ? q / (HC / 8) : 0;
+          const int c8 = ((q % (HC / 8)) ^ (rr & (HC / 8 - 1))) * 8;
+          // slot of packed row rr, selected per lane over the (uniform) slot bits so that
+          // the slot's pointer and rank come from scalar loads
+          const uint16_t *src = nullptr;
+          int rk = 1, j = 0, off = 0;
+          for (int m = slot_mask; m; m &= m - 1) {
+            const int s2 = __ffs(m) - 1;
+            const int r2 = P.rank[s2];
+            const int need = (r2 + 15) / 16 * 16;
+            if (!src && rr < off + need) {
+              src = P.down_a[s2];
+              rk = r2;
+              j = rr - off;
+            }
+            off += need;
+          }
+          j = j < rk ? j : 0;
+          const int icol = icol0 + c8 < P.I ? icol0 + c8 : 0;
+          lds_dma16(src + ((size_t)e * rk + j) * P.I + icol,
+                    __builtin_amdgcn_readfirstlane(base + (uint32_t)t * 1024u));
+        }
+      }
+    };
     auto build = [&] {
+      a2_copy();
       if (kHasExt && slot_mask) build_xs();  // visible after the main loop's first barrier
     };
     auto main_loop = [&](auto nt) {
@@ -604,8 +691,6 @@ void moe_gemm_kernel(const GemmParams P) {
       // is written out in 16-byte row chunks (the fragment layout would give 2-byte
       // stores) and, with the fused down shrink, contracted with A2 for the tile's share
       // of v = A2 . act.
-      constexpr int HC = BN / 2;      // I columns of this tile
-      constexpr int HP = HC + 8;
       static_assert(BM * HP + 64 * HP <= 2 * BN * BK, "activation tile and one A2 slice must fit LDS");
       uint16_t *Hs = reinterpret_cast<uint16_t *>(Bs);  // both B buffers are free now: [Hs | A2s]
       uint16_t *A2s = Hs + BM * HP;
@@ -620,8 +705,9 @@ void moe_gemm_kernel(const GemmParams P) {
             const int c = wn * (WTN / 2) + fh * 16 + (lane & 15);
             const float g = acc[fm][fh][i];
             const float u = acc[fm][fh + FN / 2][i];
-            Hs[r * HP + c] = (uint16_t)f32_to_bf16(silu_mul(g, u));
+            Hs[r * HP + c] = col * HC + c < P.I ? (uint16_t)f32_to_bf16(silu_mul(g, u)) : (uint16_t)0;
           }
+      if (a2_pre) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's A2 copies landed
       __syncthreads();
       for (int q = tid; q < BM * (HC / 8); q += NT) {
         const int r = q / (HC / 8), c8 = (q % (HC / 8)) * 8;
@@ -630,27 +716,40 @@ void moe_gemm_kernel(const GemmParams P) {
           *reinterpret_cast<u32x4_t *>(P.out_bf16 + (size_t)(row0 + r) * P.I + icol) =
               *reinterpret_cast<const u32x4_t *>(&Hs[r * HP + c8]);
       }
-      if (fuse_down) {
-        // A2 slices of the slots present, packed at 16-row granularity into A2s; as many
-        // slots per batch as fit, one barrier pair per batch
+      // v partials of one batch of slots (set bmask, packed rows in a2src): (row fragment,
+      // packed rank fragment) tasks over the waves
+      auto contract = [&](int bmask, int rows_used, const uint16_t *a2src, bool swizzled) {
+        const int nrf = rows_used / 16;
+        for (int f = wave; f < (BM / 16) * nrf; f += NT / 64) {
+          const int mf = f / nrf, rf = f % nrf;
+          int a, j16;
+          locate(bmask, rf * 16, a, j16);  // first rank index of this fragment
+          f32x4_t v4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < HC / 32; ++kk) {
+            const u32x4_t ha = *reinterpret_cast<const u32x4_t *>(
+                &Hs[(mf * 16 + (lane & 15)) * HP + kk * 32 + (lane >> 4) * 8]);
+            const int ar = rf * 16 + (lane & 15), ac = kk * 4 + (lane >> 4);
+            const u32x4_t hb2 = *reinterpret_cast<const u32x4_t *>(
+                &a2src[swizzled ? ar * HC + ((ac ^ (ar & (HC / 8 - 1))) << 3) : ar * HP + ac * 8]);
+            v4 = mfma_16x16x32(ha, hb2, v4);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mf * 16 + (lane >> 4) * 4 + i;
+            const int j = j16 + (lane & 15);
+            if (r < rows && j < P.rank[a] && s_slot[r] == a)
+              P.down_part[((size_t)col * P.R + row0 + r) * P.rmax + j] = v4[i];
+          }
+        }
+      };
+      if (a2_pre) {
+        contract(slot_mask, a2_rows, A2p, true);  // A2 copied in with the first K steps
+      } else if (fuse_down) {
+        // slots whose A2 rows did not fit the prefetch region: A2 slices packed into A2s,
+        // as many slots per batch as fit, one barrier pair per batch
         constexpr int kCapRows = ((2 * BN * BK - BM * HP) / HP) / 16 * 16;
         const int icol0 = col * HC;
-        // packed row rr of a batch (slot set bmask) -> (slot, rank index); loops over the
-        // slot bits instead of indexing per-batch arrays, which would live in scratch
-        auto locate = [&](int bmask, int rr, int &a, int &j) {
-          a = -1;
-          j = 0;
-          int off = 0;
-          for (int m = bmask; m; m &= m - 1) {
-            const int s = __ffs(m) - 1;
-            const int need = (P.rank[s] + 15) / 16 * 16;
-            if (a < 0 && rr < off + need) {
-              a = s;
-              j = rr - off;
-            }
-            off += need;
-          }
-        };
         int pending = slot_mask;
         while (pending) {
           int bmask = 0, rows_used = 0;
@@ -662,7 +761,7 @@ void moe_gemm_kernel(const GemmParams P) {
             rows_used += need;
             pending &= pending - 1;
           }
-          __syncthreads();  // Hs written / previous batch's reads of A2s done
+          __syncthreads();  // previous batch's reads of A2s done
           for (int q = tid; q < rows_used * (HC / 8); q += NT) {
             const int rr = q / (HC / 8), c8 = (q % (HC / 8)) * 8;
             int a, j;
@@ -674,29 +773,7 @@ void moe_gemm_kernel(const GemmParams P) {
             *reinterpret_cast<u32x4_t *>(&A2s[rr * HP + c8]) = v;
           }
           __syncthreads();
-          // (row fragment, packed rank fragment) tasks over the waves
-          const int nrf = rows_used / 16;
-          for (int f = wave; f < (BM / 16) * nrf; f += NT / 64) {
-            const int mf = f / nrf, rf = f % nrf;
-            int a, j16;
-            locate(bmask, rf * 16, a, j16);  // first rank index of this fragment
-            f32x4_t v4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < HC / 32; ++kk) {
-              const u32x4_t ha = *reinterpret_cast<const u32x4_t *>(
-                  &Hs[(mf * 16 + (lane & 15)) * HP + kk * 32 + (lane >> 4) * 8]);
-              const u32x4_t hb2 = *reinterpret_cast<const u32x4_t *>(
-                  &A2s[(rf * 16 + (lane & 15)) * HP + kk * 32 + (lane >> 4) * 8]);
-              v4 = mfma_16x16x32(ha, hb2, v4);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = mf * 16 + (lane >> 4) * 4 + i;
-              const int j = j16 + (lane & 15);
-              if (r < rows && j < P.rank[a] && s_slot[r] == a)
-                P.down_part[((size_t)col * P.R + row0 + r) * P.rmax + j] = v4[i];
-            }
-          }
+          contract(bmask, rows_used, A2s, false);
         }
       }
     } else if constexpr (MODE == MODE_DOWN) {
