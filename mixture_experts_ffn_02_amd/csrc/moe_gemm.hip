@@ -138,6 +138,14 @@ void moe_gemm_kernel(const GemmParams P) {
   constexpr int kA2Rows = 128;
   static_assert((kA2Rows * HC / 8) % 64 == 0, "A2 region must be whole wave copies");
   __shared__ __attribute__((aligned(16))) uint16_t A2p[kA2Pre ? kA2Rows * HC : 8];
+  // Decode-height tiles whose rows all use one adapter slot of rank <= 32 (a multiple of
+  // 8): that slot's B rows for the tile's BN output columns, copied into LDS when the tile
+  // starts (32 ranks per row, 16-byte chunks XOR-swizzled by row / 4), so the expand step
+  // does not wait a memory round trip behind the weight stream at the end of the tile.
+  constexpr bool kExtLds = kHasExt && kHasMain && BM <= 16;
+  constexpr int kEbRank = 32;
+  static_assert(!kExtLds || (BN * kEbRank / 8) % 64 == 0, "expand B region must be whole wave copies");
+  __shared__ __attribute__((aligned(16))) uint16_t Eb[kExtLds ? BN * kEbRank : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -547,7 +555,11 @@ void moe_gemm_kernel(const GemmParams P) {
     }
     const int full = kHasMain ? P.K / BK : 0;
     constexpr bool kExtEarly = kHasExt && kHasMain;
-    const bool ext_early = kExtEarly && slot_mask != 0 && r8 && full >= PF && full % PF == 0 && full * BK == P.K;
+    const int slot1 = slot_mask ? __ffs(slot_mask) - 1 : 0;
+    const bool ext_lds = kExtLds && slot_mask != 0 && (slot_mask & (slot_mask - 1)) == 0 &&
+                         (P.rank[slot1] & 7) == 0 && P.rank[slot1] <= kEbRank;
+    const bool ext_early = kExtEarly && !ext_lds && slot_mask != 0 && r8 && full >= PF && full % PF == 0 &&
+                           full * BK == P.K;
     auto load_ext_b_clamped = [&](int a, u32x4_t(&xb)[B_IT]) {
       const int ra_rank = P.rank[a];
       const uint16_t *bl = P.lora_w[a];
@@ -616,7 +628,35 @@ void moe_gemm_kernel(const GemmParams P) {
         }
       }
     };
+    // the single slot's B rows into Eb (LDS row n = B row of output column n of the tile,
+    // physical chunk p of a row holds ranks 8 * (p ^ ((n >> 2) & 3)) ..; chunks past the
+    // rank read a valid element, which meets zeros in Xs)
+    auto eb_copy = [&] {
+      if constexpr (kExtLds) {
+        if (!ext_lds) return;
+        const int rk = P.rank[slot1];
+        const uint16_t *bl = P.lora_w[slot1];
+        const uint32_t base = lds_addr(Eb);
+        for (int t = wave; t < BN * kEbRank / 8 / 64; t += NT / 64) {
+          const int n = t * 16 + (lane >> 2);
+          const int c8 = ((lane & 3) ^ ((n >> 2) & 3)) * 8;
+          int wr;
+          if (kGateUp) {
+            const int wnn = n / WTN, ccw = n % WTN;
+            const int half = ccw / (WTN / 2), j = ccw % (WTN / 2);
+            const int icol = col * (BN / 2) + wnn * (WTN / 2) + j;
+            wr = icol < P.I ? half * P.I + icol : 0;
+          } else {
+            const int ng = col * BN + n;
+            wr = ng < P.N ? ng : 0;
+          }
+          lds_dma16(bl + ((size_t)e * P.N + wr) * rk + (c8 < rk ? c8 : 0),
+                    __builtin_amdgcn_readfirstlane(base + (uint32_t)t * 1024u));
+        }
+      }
+    };
     auto build = [&] {
+      eb_copy();
       a2_copy();
       if (kHasExt && slot_mask) build_xs();  // visible after the main loop's first barrier
     };
@@ -644,7 +684,25 @@ void moe_gemm_kernel(const GemmParams P) {
     } else {
       build();
     }
-    if (kHasExt && slot_mask) {
+    if (kExtLds && ext_lds) {
+      // one K step over ranks 0-31: A fragments from Xs (rows of other slots or none are
+      // zero there), B fragments from Eb
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's B copies landed
+      __syncthreads();
+      u32x4_t af[FM], bfr[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        af[fm] = *reinterpret_cast<const u32x4_t *>(&Xs[(wm * WTM + fm * 16) * BK + frag_lane[0]]);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int n = wn * WTN + fn * 16 + (lane & 15);
+        bfr[fn] = *reinterpret_cast<const u32x4_t *>(&Eb[n * kEbRank + (((lane >> 4) ^ ((n >> 2) & 3)) << 3)]);
+      }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32(af[fm], bfr[fn], acc[fm][fn]);
+    } else if (kHasExt && slot_mask) {
       // B operands of up to PF slots loaded at once into the (now idle) register stages,
       // then one masked K step per slot with A fragments read from Xs
       pending = slot_mask;
