@@ -20,11 +20,11 @@
 // B operand is the slot's B matrix (rows masked to the tile rows of that slot).
 //
 // Tiling: BM token rows x BN weight rows per workgroup, BK = 64, both operands staged
-// through double-buffered LDS (row pitch 72 elements so that the 16-byte fragment reads
-// of 16 consecutive rows fall in distinct banks), v_mfma_f32_16x16x32_bf16 on 64-wide
-// wavefronts.  Work tiles are (expert, m-tile, n-tile) triples found on the device from
-// expert_offsets; block ids are remapped so each XCD runs a contiguous range of them,
-// keeping an expert's weight and activation tiles in that XCD's L2.
+// through double-buffered LDS (unpadded 128-byte rows, 16-byte chunks XOR-swizzled by
+// row), v_mfma_f32_16x16x32_bf16 on 64-wide wavefronts.  Work tiles are (expert,
+// m-tile, n-tile) triples found on the device from expert_offsets; block ids are
+// remapped so each XCD runs a contiguous range of them, keeping an expert's weight and
+// activation tiles in that XCD's L2.
 #include <type_traits>
 
 #include "common.h"
