@@ -212,6 +212,23 @@ def main():
         torch.cuda.synchronize()
         t_two = (time.perf_counter() - t0) / n2
 
+    t_graph = None
+    if cfg.T <= 256:
+        log("timing LoRA on, replays of one captured HIP graph of the step")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer(x, logits, lora)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        t_graph = (time.perf_counter() - t0) / args.steps
+        del graph
+
     # realized routing -> algorithmic bytes and flops
     layer(x, logits, lora)
     torch.cuda.synchronize()
@@ -276,6 +293,7 @@ def main():
         "ms_per_step_lora_off": round(t_off * 1e3, 4),
         "ms_per_step_explicit_permute": round(t_perm * 1e3, 4),
         "ms_per_step_two_stream": round(t_two * 1e3, 4) if t_two else None,
+        "ms_per_step_graph_replay": round(t_graph * 1e3, 4) if t_graph else None,
         "layer_roofline": {
             "algorithmic_bytes": int(layer_bytes), "algorithmic_flops": int(layer_flops),
             "active_experts": active,

@@ -158,8 +158,8 @@ class MoELoRALayer:
                 "off": torch.empty((self.E + 1,), **i32),
                 "e2p": torch.empty((R,), **i32),
                 "p2e": torch.empty((R,), **i32),
-                # zeroed once: its head is the routing kernel's arrival counter
-                "rws": torch.zeros((max(1, moe_lora_route_workspace_size(d)),), dtype=torch.uint8,
+                # per-workgroup expert histograms of the two-launch routing (written before read)
+                "rws": torch.empty((max(1, moe_lora_route_workspace_size(d)),), dtype=torch.uint8,
                                    device=device),
                 "fws": torch.empty((max(1, moe_lora_forward_workspace_size(d, lora)),),
                                    dtype=torch.uint8, device=device),
