@@ -18,5 +18,6 @@ from .moe_lora_ref import (  # noqa: F401
     route,
     route_deepseek_v3,
     route_renormalize,
+    shared_outer_adapter,
     silu,
 )

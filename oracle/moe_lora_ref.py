@@ -42,6 +42,9 @@ Readings of points the pages leave open (each is also listed in the design notes
     contributions scale together.
   * a token whose slot is outside [0, num_slots) gets no LoRA (the pages' -1
     sentinel for "no adapter").
+  * shared-outer LoRA ([P1] section 2): the gate_up A and the down B are shared by all
+    experts, the gate_up B and the down A are per expert; rounding and weighting as in
+    the routed layer (the down delta is added to the expert output before finalize).
 """
 
 from __future__ import annotations
@@ -173,6 +176,21 @@ class Adapter:
     b_gate_up: BitsFn
     a_down: BitsFn
     b_down: BitsFn
+
+
+def shared_outer_adapter(rank: int, scaling: float, a_gate_up: np.ndarray, b_gate_up: BitsFn,
+                         a_down: BitsFn, b_down: np.ndarray) -> Adapter:
+    """A shared-outer LoRA slot ([P1] section 2, "Shared-outer LoRA"): the gate_up A
+    ([r, H]) and the down B ([H, r]) are one weight set that every expert uses (selected
+    by the adapter alone), while the gate_up B and the down A stay per expert:
+
+        g = W1[e] x + s_a B1[a][e] (A1[a] x)
+        y = W2[e] h + s_a B2[a] (A2[a][e] h)
+
+    The layer is otherwise the routed one, so the slot is an Adapter whose A1 and B2
+    getters ignore the expert index.
+    """
+    return Adapter(rank, scaling, lambda e: a_gate_up, b_gate_up, a_down, lambda e: b_down)
 
 
 def _valid_slot(slot: np.ndarray, num_slots: int) -> np.ndarray:

@@ -44,6 +44,8 @@ _T_A1 = 20
 _T_B1 = 21
 _T_A2 = 22
 _T_B2 = 23
+_T_A1_SHARED = 24
+_T_B2_SHARED = 25
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -231,6 +233,15 @@ class Workload:
     def lora_b_down(self, a: int, e: int) -> np.ndarray:
         c = self.cfg
         return self._normal_bf16((c.H, c.slots[a].rank), c.lora_b_std, _T_B2, a, e)
+
+    # shared-outer layout: one gate_up A and one down B per slot for all experts
+    def lora_a_gate_up_shared(self, a: int) -> np.ndarray:
+        c = self.cfg
+        return self._normal_bf16((c.slots[a].rank, c.H), c.lora_a_std, _T_A1_SHARED, a)
+
+    def lora_b_down_shared(self, a: int) -> np.ndarray:
+        c = self.cfg
+        return self._normal_bf16((c.H, c.slots[a].rank), c.lora_b_std, _T_B2_SHARED, a)
 
     # -- stacked forms ---------------------------------------------------
     def _stack(self, fn, count: int, shape, experts: Optional[Sequence[int]] = None) -> np.ndarray:

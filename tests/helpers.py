@@ -7,10 +7,17 @@ import numpy as np
 import oracle
 
 
-def oracle_adapters(wl):
+def oracle_adapters(wl, shared_outer=False):
     cfg = wl.cfg
     ads = []
     for a, sp in enumerate(cfg.slots):
+        if shared_outer:
+            ads.append(oracle.shared_outer_adapter(
+                sp.rank, sp.scaling, wl.lora_a_gate_up_shared(a),
+                functools.lru_cache(None)(lambda e, a=a: wl.lora_b_gate_up(a, e)),
+                functools.lru_cache(None)(lambda e, a=a: wl.lora_a_down(a, e)),
+                wl.lora_b_down_shared(a)))
+            continue
         ads.append(oracle.Adapter(
             rank=sp.rank, scaling=sp.scaling,
             a_gate_up=functools.lru_cache(None)(lambda e, a=a: wl.lora_a_gate_up(a, e)),

@@ -228,3 +228,54 @@ def test_sampled_layer_equals_full_layer():
     got = oracle.layer_sampled(wl.x(), res["ids"], res["weights"], toks, SMALL.I, wl.w_gate_up,
                                wl.w_down, ads, wl.token_slot())
     np.testing.assert_allclose(got, res["out"][toks], rtol=1e-13, atol=1e-15)
+
+
+def _merged_shared_outer_reference(wl):
+    """Base MoE on merged weights for shared-outer slots, W1' = W1[e] + s B1[a][e] A1[a]
+    and W2' = W2[e] + s B2[a] A2[a][e], written directly with numpy per routed pair."""
+    cfg = wl.cfg
+    x = _f(wl.x())
+    ids, w = oracle.route(wl.logits(), cfg.top_k, cfg.routing, wl.correction_bias(), cfg.n_group,
+                          cfg.topk_group, cfg.routed_scaling_factor)
+    slots = wl.token_slot()
+    out = np.zeros((cfg.T, cfg.H))
+    cache = {}
+    for t in range(cfg.T):
+        a = int(slots[t])
+        for j in range(cfg.top_k):
+            e = int(ids[t, j])
+            key = (e, a if 0 <= a < cfg.num_slots else -1)
+            if key not in cache:
+                W1 = _f(wl.w_gate_up(e))
+                W2 = _f(wl.w_down(e))
+                if key[1] >= 0:
+                    s = cfg.slots[a].scaling
+                    W1 = W1 + s * _f(wl.lora_b_gate_up(a, e)) @ _f(wl.lora_a_gate_up_shared(a))
+                    W2 = W2 + s * _f(wl.lora_b_down_shared(a)) @ _f(wl.lora_a_down(a, e))
+                cache[key] = (W1, W2)
+            W1, W2 = cache[key]
+            g = W1 @ x[t]
+            h = g[: cfg.I] / (1.0 + np.exp(-g[: cfg.I])) * g[cfg.I:]
+            out[t] += w[t, j] * (W2 @ h)
+    return out
+
+
+@pytest.mark.parametrize("cfg", [SMALL, NAMED_CONFIGS[1],
+                                 dataclasses.replace(NAMED_CONFIGS[4], T=12, H=256, I=128, E=16)])
+def test_shared_outer_lora_equals_merged_weights(cfg):
+    """Shared-outer slots (gate_up A and down B shared by the experts) against the merged
+    weights of the same slots."""
+    wl = Workload(cfg)
+    got = oracle_layer(wl, adapters=oracle_adapters(wl, shared_outer=True))["out"]
+    want = _merged_shared_outer_reference(wl)
+    assert rel_l2(got, want) < 1e-12
+    np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12)
+
+
+def test_shared_outer_differs_from_routed_and_from_base():
+    """The shared weights are used: the output moves away from both the routed-LoRA and
+    the base layer by far more than the layer tolerance."""
+    wl = Workload(SMALL)
+    shared = oracle_layer(wl, adapters=oracle_adapters(wl, shared_outer=True))["out"]
+    assert rel_l2(shared, oracle_layer(wl)["out"]) > 0.05
+    assert rel_l2(shared, oracle_layer(wl, with_lora=False)["out"]) > 0.05
