@@ -212,6 +212,16 @@ def main():
         torch.cuda.synchronize()
         t_two = (time.perf_counter() - t0) / n2
 
+    t_shared = None
+    if lora is not None:
+        log("timing LoRA on, shared-outer layout (one gate_up A and one down B per slot)")
+        lora_so = ml.LoRASlots(lora.token_slot, lora.rank, lora.scaling,
+                               [t16(wl.lora_a_gate_up_shared(a)) for a in range(cfg.num_slots)],
+                               lora.b_gate_up, lora.a_down,
+                               [t16(wl.lora_b_down_shared(a)) for a in range(cfg.num_slots)],
+                               shared_outer=True)
+        t_shared, _ = timed(layer, lora_so, max(5, args.steps // 2), args.warmup)
+
     t_graph = None
     if cfg.T <= 256:
         log("timing LoRA on, replays of one captured HIP graph of the step")
@@ -294,6 +304,8 @@ def main():
         "ms_per_step_explicit_permute": round(t_perm * 1e3, 4),
         "ms_per_step_two_stream": round(t_two * 1e3, 4) if t_two else None,
         "ms_per_step_graph_replay": round(t_graph * 1e3, 4) if t_graph else None,
+        "shared_outer": ({"ms_per_step": round(t_shared * 1e3, 4), "value": round(T / t_shared, 1),
+                          "lora_ratio": round(t_off / t_shared, 4)} if t_shared else None),
         "layer_roofline": {
             "algorithmic_bytes": int(layer_bytes), "algorithmic_flops": int(layer_flops),
             "active_experts": active,

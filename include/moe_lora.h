@@ -101,6 +101,11 @@ typedef struct {
   const uint16_t *b_gate_up[MOE_LORA_MAX_SLOTS];
   const uint16_t *a_down[MOE_LORA_MAX_SLOTS];
   const uint16_t *b_down[MOE_LORA_MAX_SLOTS];
+  /* 0: the routed layout above.  1: shared-outer LoRA (bf16 PR, section 2 "Shared-outer
+   * LoRA"): the gate_up A and the down B are one weight set per slot that every expert
+   * uses, a_gate_up[s]: [rank[s], H] and b_down[s]: [H, rank[s]]; b_gate_up and a_down
+   * keep their per-expert layouts.  Other values -> MOE_LORA_ERR_INVALID_ARGUMENT. */
+  int32_t shared_outer;
 } moe_lora_adapters;
 
 /* Optional knobs of moe_lora_forward (NULL = defaults). */

@@ -54,7 +54,8 @@ class Adapters(ctypes.Structure):
     _fields_ = [("num_slots", c_int32), ("token_slot", c_void_p),
                 ("rank", c_int32 * MAX_SLOTS), ("scaling", c_float * MAX_SLOTS),
                 ("a_gate_up", c_void_p * MAX_SLOTS), ("b_gate_up", c_void_p * MAX_SLOTS),
-                ("a_down", c_void_p * MAX_SLOTS), ("b_down", c_void_p * MAX_SLOTS)]
+                ("a_down", c_void_p * MAX_SLOTS), ("b_down", c_void_p * MAX_SLOTS),
+                ("shared_outer", c_int32)]
 
 
 class Options(ctypes.Structure):

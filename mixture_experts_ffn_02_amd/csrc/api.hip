@@ -25,6 +25,7 @@ int check_dims(const moe_lora_dims *d) {
 int check_lora_shape(const moe_lora_adapters *l) {
   if (!l) return MOE_LORA_OK;
   if (l->num_slots < 0 || l->num_slots > MOE_LORA_MAX_SLOTS) return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (l->shared_outer != 0 && l->shared_outer != 1) return MOE_LORA_ERR_INVALID_ARGUMENT;
   for (int s = 0; s < l->num_slots; ++s) {
     if (l->rank[s] <= 0) return MOE_LORA_ERR_INVALID_ARGUMENT;
     if (l->rank[s] > MOE_LORA_MAX_RANK) return MOE_LORA_ERR_UNSUPPORTED;

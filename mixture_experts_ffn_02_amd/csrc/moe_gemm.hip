@@ -80,6 +80,7 @@ struct GemmParams {
   int rank[MOE_LORA_MAX_SLOTS];
   float scaling[MOE_LORA_MAX_SLOTS];
   const uint16_t *lora_w[MOE_LORA_MAX_SLOTS];  // SHRINK: A [E, r, K]; ext: B [E, N, r]
+  int lora_w_shared;  // lora_w holds one matrix per slot for all experts (shared-outer)
   const float *part;                            // ext A source [splits][R][rmax]
   int part_splits;
   int rmax;
@@ -363,7 +364,7 @@ void moe_gemm_kernel(const GemmParams P) {
       const int wr = b_wrow[i];
       const int j0 = b_c8[i] * 8;
       if (wr >= 0 && j0 < ra_rank) {
-        const uint16_t *srcb = bl + ((size_t)e * P.N + wr) * ra_rank + j0;
+        const uint16_t *srcb = bl + ((size_t)(P.lora_w_shared ? 0 : e) * P.N + wr) * ra_rank + j0;
         if ((ra_rank & 7) == 0) {
           xb[i] = *reinterpret_cast<const u32x4_t *>(srcb);
         } else {
@@ -514,7 +515,7 @@ void moe_gemm_kernel(const GemmParams P) {
     for (int a = col % groups; a < P.num_slots; a += groups) {
       if (!((slot_mask >> a) & 1)) continue;
       const int r_a = P.rank[a];
-      const uint16_t *bbase = P.lora_w[a] + (size_t)e * r_a * P.K;
+      const uint16_t *bbase = P.lora_w[a] + (size_t)(P.lora_w_shared ? 0 : e) * r_a * P.K;
       zero_acc();
       run_full(s0, s1f, bbase, r_a, [] {}, [](int) {}, std::false_type{});
       if (s1 > s1f) run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
@@ -571,7 +572,8 @@ void moe_gemm_kernel(const GemmParams P) {
       for (int i = 0; i < B_IT; ++i) {
         const int wr = b_wrow[i] >= 0 ? b_wrow[i] : 0;
         const int j0 = b_c8[i] * 8 < ra_rank ? b_c8[i] * 8 : 0;
-        xb[i] = *reinterpret_cast<const u32x4_t *>(bl + ((size_t)e_late * P.N + wr) * ra_rank + j0);
+        xb[i] = *reinterpret_cast<const u32x4_t *>(
+            bl + ((size_t)(P.lora_w_shared ? 0 : e_late) * P.N + wr) * ra_rank + j0);
       }
     };
     // packed row rr of the slot set bmask -> (slot, rank index); loops over the slot bits
@@ -650,7 +652,7 @@ void moe_gemm_kernel(const GemmParams P) {
             const int ng = col * BN + n;
             wr = ng < P.N ? ng : 0;
           }
-          lds_dma16(bl + ((size_t)e * P.N + wr) * rk + (c8 < rk ? c8 : 0),
+          lds_dma16(bl + ((size_t)(P.lora_w_shared ? 0 : e) * P.N + wr) * rk + (c8 < rk ? c8 : 0),
                     __builtin_amdgcn_readfirstlane(base + (uint32_t)t * 1024u));
         }
       }
@@ -1141,6 +1143,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     shrink1.N = 0;
     shrink1.k_steps_per_split = L.steps1;
     for (int s = 0; s < lora->num_slots; ++s) shrink1.lora_w[s] = lora->a_gate_up[s];
+    shrink1.lora_w_shared = lora->shared_outer;  // shared-outer: one A1 for all experts
     shrink1.out_f32 = u_part;
     shrink1.row_slot_out = row_slot;
   }
@@ -1229,6 +1232,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     P.N = d.hidden;
     if (has_lora) {
       for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->b_down[s];
+      P.lora_w_shared = lora->shared_outer;  // shared-outer: one B2 for all experts
       P.part = v_part;
       P.part_splits = decomposed ? L.shrink2_splits : gateup_ncols(bm, d.inter);
       P.row_slot = row_slot;

@@ -42,15 +42,20 @@ def dims(num_tokens: int, hidden: int, inter: int, num_experts: int, top_k: int)
 
 @dataclass
 class LoRASlots:
-    """Resident adapter slots (per-slot compact weights, device tensors)."""
+    """Resident adapter slots (per-slot compact weights, device tensors).
+
+    shared_outer: the shared-outer layout, where a_gate_up[s] is [r, H] and b_down[s] is
+    [H, r], one set used by every expert (b_gate_up and a_down stay per expert).
+    """
 
     token_slot: torch.Tensor  # [T] int32
     rank: Sequence[int]
     scaling: Sequence[float]
-    a_gate_up: Sequence[torch.Tensor]  # [E, r, H]
+    a_gate_up: Sequence[torch.Tensor]  # [E, r, H]  (shared-outer: [r, H])
     b_gate_up: Sequence[torch.Tensor]  # [E, 2I, r]
     a_down: Sequence[torch.Tensor]     # [E, r, I]
-    b_down: Sequence[torch.Tensor]     # [E, H, r]
+    b_down: Sequence[torch.Tensor]     # [E, H, r]  (shared-outer: [H, r])
+    shared_outer: bool = False
 
     def to_c(self) -> Adapters:
         n = len(self.rank)
@@ -59,6 +64,7 @@ class LoRASlots:
         a = Adapters()
         a.num_slots = n
         a.token_slot = _ptr(self.token_slot)
+        a.shared_outer = 1 if self.shared_outer else 0
         for s in range(n):
             a.rank[s] = int(self.rank[s])
             a.scaling[s] = float(self.scaling[s])

@@ -105,9 +105,15 @@ class GpuLayer:
             c[e] = self.wl.w_down(e)
         return c[e]
 
-    def oracle_adapters(self):
+    def oracle_adapters(self, shared_outer: bool = False):
         ads = []
         for a, sp in enumerate(self.cfg.slots):
+            if shared_outer:
+                d = self.lora_np[a]
+                ads.append(oracle.shared_outer_adapter(
+                    sp.rank, sp.scaling, self.wl.lora_a_gate_up_shared(a), lambda e, d=d: d["b_gate_up"][e],
+                    lambda e, d=d: d["a_down"][e], self.wl.lora_b_down_shared(a)))
+                continue
             d = self.lora_np[a]
             ads.append(oracle.Adapter(sp.rank, sp.scaling,
                                       lambda e, d=d: d["a_gate_up"][e], lambda e, d=d: d["b_gate_up"][e],
@@ -125,7 +131,11 @@ class GpuLayer:
         return ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, self.w1, self.w2, self.routing, c.n_group,
                                c.topk_group, c.routed_scaling_factor, self.bias, gather_on_load)
 
-    def lora_slots(self, token_slot: Optional[np.ndarray] = None, zero_b: bool = False):
+    def lora_slots(self, token_slot: Optional[np.ndarray] = None, zero_b: bool = False,
+                   shared_outer: bool = False, replicate_shared: bool = False):
+        """Device adapter slots.  shared_outer: the shared-outer layout (one gate_up A and
+        one down B per slot); replicate_shared: the same weights in the routed layout, the
+        shared matrices copied for every expert."""
         c = self.cfg
         if c.num_slots == 0:
             return None
@@ -133,6 +143,13 @@ class GpuLayer:
         L = self.lora_t
         bg = [torch.zeros_like(d["b_gate_up"]) if zero_b else d["b_gate_up"] for d in L]
         bd = [torch.zeros_like(d["b_down"]) if zero_b else d["b_down"] for d in L]
+        ag = [d["a_gate_up"] for d in L]
+        if shared_outer or replicate_shared:
+            ag = [t16(self.wl.lora_a_gate_up_shared(a)) for a in range(c.num_slots)]
+            bd = [t16(self.wl.lora_b_down_shared(a)) for a in range(c.num_slots)]
+            if replicate_shared:
+                ag = [t.unsqueeze(0).expand(c.E, *t.shape).contiguous() for t in ag]
+                bd = [t.unsqueeze(0).expand(c.E, *t.shape).contiguous() for t in bd]
         return ml.LoRASlots(torch.from_numpy(np.ascontiguousarray(ts, dtype=np.int32)).to(dev()),
                             [s.rank for s in c.slots], [s.scaling for s in c.slots],
-                            [d["a_gate_up"] for d in L], bg, [d["a_down"] for d in L], bd)
+                            ag, bg, [d["a_down"] for d in L], bd, shared_outer=shared_outer)

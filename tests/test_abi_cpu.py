@@ -24,6 +24,21 @@ def test_header_and_binding_agree():
     assert _declared() == sorted(_lib.EXPORTED)
 
 
+def _struct_fields(name):
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\}\s*" + name + ";", src).group(1)
+    return [re.search(r"(\w+)\s*(\[[^\]]*\])?\s*;", f.strip()).group(1)
+            for f in body.split(";") if f.strip() for f in [f + ";"]]
+
+
+@pytest.mark.parametrize("cname,ctype", [("moe_lora_dims", _lib.Dims), ("moe_lora_grouped", _lib.Grouped),
+                                         ("moe_lora_adapters", _lib.Adapters),
+                                         ("moe_lora_options", _lib.Options)])
+def test_struct_layouts_agree(cname, ctype):
+    """The binding's ctypes structures list the header's fields in the header's order."""
+    assert [f[0] for f in ctype._fields_] == _struct_fields(cname)
+
+
 def test_library_exports_every_declared_symbol():
     lib = pkg.load()
     for name in _declared():
@@ -137,6 +152,11 @@ def test_forward_argument_checks():
     o.force_path = -1
     assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
                                 None, ctypes.byref(o)) == _lib.ERR_INVALID_ARGUMENT
+    # shared_outer is a flag
+    a.shared_outer = 2
+    assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
+                                None, None) == _lib.ERR_INVALID_ARGUMENT
+    a.shared_outer = 0
     a.b_down[0] = None
     assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
                                 None, None) == _lib.ERR_INVALID_ARGUMENT
