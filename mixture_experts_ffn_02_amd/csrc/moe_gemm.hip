@@ -139,11 +139,13 @@ void moe_gemm_kernel(const GemmParams P) {
   constexpr int kA2Rows = 128;
   static_assert((kA2Rows * HC / 8) % 64 == 0, "A2 region must be whole wave copies");
   __shared__ __attribute__((aligned(16))) uint16_t A2p[kA2Pre ? kA2Rows * HC : 8];
-  // Decode-height tiles whose rows all use one adapter slot of rank <= 32 (a multiple of
-  // 8): that slot's B rows for the tile's BN output columns, copied into LDS when the tile
-  // starts (32 ranks per row, 16-byte chunks XOR-swizzled by row / 4), so the expand step
-  // does not wait a memory round trip behind the weight stream at the end of the tile.
-  constexpr bool kExtLds = kHasExt && kHasMain && BM <= 16;
+  // Tiles whose rows all use one adapter slot of rank <= 32 (a multiple of 8): that slot's
+  // B rows for the tile's BN output columns, copied into LDS when the tile starts (32
+  // ranks per row, 16-byte chunks XOR-swizzled by row / 4), so the expand is one unmasked
+  // 32-wide K step from LDS instead of a register-staged step that waits for its loads
+  // at the end of the tile.  Decode-height tiles and the 64-row down GEMM have the LDS
+  // for it (on the 128x256 down tile the extra addressing spilled in the K loop).
+  constexpr bool kExtLds = kHasExt && kHasMain && (BM <= 16 || (MODE == MODE_DOWN && BM <= 64));
   constexpr int kEbRank = 32;
   static_assert(!kExtLds || (BN * kEbRank / 8) % 64 == 0, "expand B region must be whole wave copies");
   __shared__ __attribute__((aligned(16))) uint16_t Eb[kExtLds ? BN * kEbRank : 8];
@@ -383,15 +385,18 @@ void moe_gemm_kernel(const GemmParams P) {
     for (int i = 0; i < B_IT; ++i) *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = xb[i];
   };
   // one 64-wide K step of the expand: A rows from Xs masked to the rows of slot a
-  auto compute_ext = [&](int buf, int a) {
+  // (ranks past rmax are zero in Xs, so the second 32-wide half is skipped when rmax <= 32;
+  // with one slot in the tile, rows of no slot are zero in Xs and need no mask)
+  auto compute_ext = [&](int buf, int a, bool masked) {
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
+      if (kk > 0 && P.rmax <= 32) break;
       u32x4_t af[FM], bfr[FN];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int r = wm * WTM + fm * 16 + (lane & 15);
         af[fm] = *reinterpret_cast<const u32x4_t *>(&Xs[(wm * WTM + fm * 16) * BK + frag_lane[kk]]);
-        if (s_slot[r] != a) af[fm] = zero_u32x4();
+        if (masked && s_slot[r] != a) af[fm] = zero_u32x4();
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
@@ -740,7 +745,7 @@ void moe_gemm_kernel(const GemmParams P) {
           if (batch[u] < 0) continue;
           store_b(u & 1, rb[u]);
           __syncthreads();
-          compute_ext(u & 1, batch[u]);
+          compute_ext(u & 1, batch[u], (slot_mask & (slot_mask - 1)) != 0);
           __syncthreads();
         }
       }
