@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--only-lora-on", action="store_true",
                     help="run only the LoRA-on leg (for counter collection)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--weights", choices=("packed", "row-major"), default="packed",
+                    help="expert weight layout the GEMMs read (packed once before timing)")
     return ap.parse_args()
 
 
@@ -151,10 +153,17 @@ def main():
     w2 = stack_to_device("w_down", (cfg.H, cfg.I))
     lora_t = [{k: t16(v) for k, v in wl.lora_all(a).items()} for a in range(cfg.num_slots)]
     routing = ml.ROUTING_DEEPSEEK_V3 if cfg.routing == "deepseek_v3" else ml.ROUTING_RENORMALIZE
+    packed = args.weights == "packed"
     layer = ml.MoELoRALayer(cfg.H, cfg.I, cfg.E, cfg.top_k, w1, w2, routing, cfg.n_group,
-                            cfg.topk_group, cfg.routed_scaling_factor, bias, gather_on_load=True)
-    layer_p = ml.MoELoRALayer(cfg.H, cfg.I, cfg.E, cfg.top_k, w1, w2, routing, cfg.n_group,
-                              cfg.topk_group, cfg.routed_scaling_factor, bias, gather_on_load=False)
+                            cfg.topk_group, cfg.routed_scaling_factor, bias, gather_on_load=True,
+                            packed_weights=packed)
+    # the same weights in the row-major layout, for the bench line's comparison leg
+    layer_rm = ml.MoELoRALayer(cfg.H, cfg.I, cfg.E, cfg.top_k, w1, w2, routing, cfg.n_group,
+                               cfg.topk_group, cfg.routed_scaling_factor, bias,
+                               gather_on_load=True) if packed else None
+    layer_p = ml.MoELoRALayer(cfg.H, cfg.I, cfg.E, cfg.top_k, layer.w_gate_up, layer.w_down, routing,
+                              cfg.n_group, cfg.topk_group, cfg.routed_scaling_factor, bias,
+                              gather_on_load=False, weights_prepacked=packed)
     lora = ml.LoRASlots(torch.from_numpy(slots_np).to(dev), [s.rank for s in cfg.slots],
                         [s.scaling for s in cfg.slots], [d["a_gate_up"] for d in lora_t],
                         [d["b_gate_up"] for d in lora_t], [d["a_down"] for d in lora_t],
@@ -211,6 +220,11 @@ def main():
             layer(x, logits, lora, side_stream=side)
         torch.cuda.synchronize()
         t_two = (time.perf_counter() - t0) / n2
+
+    t_rm = None
+    if layer_rm is not None:
+        log("timing LoRA on with the row-major weight layout")
+        t_rm, _ = timed(layer_rm, lora, max(5, args.steps // 2), args.warmup)
 
     t_shared = None
     if lora is not None:
@@ -297,13 +311,15 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,sigma) bf16 tensors of the workload's shapes; no checkpoint)",
         "config": {"workload": cfg.name, **cfg.describe(), "parallelism": "single GPU",
-                   "permute": "gathered inside the GEMM and shrink loads"},
+                   "permute": "gathered inside the GEMM and shrink loads",
+                   "weights": "tile-packed once before timing" if packed else "row-major"},
         "lora_off_value": round(tok_off, 1),
         "lora_ratio": round(tok_on / tok_off, 4),
         "ms_per_step_lora_off": round(t_off * 1e3, 4),
         "ms_per_step_explicit_permute": round(t_perm * 1e3, 4),
         "ms_per_step_two_stream": round(t_two * 1e3, 4) if t_two else None,
         "ms_per_step_graph_replay": round(t_graph * 1e3, 4) if t_graph else None,
+        "ms_per_step_row_major_weights": round(t_rm * 1e3, 4) if t_rm else None,
         "shared_outer": ({"ms_per_step": round(t_shared * 1e3, 4), "value": round(T / t_shared, 1),
                           "lora_ratio": round(t_off / t_shared, 4)} if t_shared else None),
         "layer_roofline": {

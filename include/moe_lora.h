@@ -116,7 +116,12 @@ typedef struct {
    * after the gate_up GEMM launch, so a caller can time that kernel alone. */
   void *gate_up_event_begin;
   void *gate_up_event_end;
-  int32_t reserved[4];
+  /* 1: w_gate_up and w_down are the tile-packed copies written by
+   * moe_lora_pack_weights (hidden % 128 == 0 and inter % 64 == 0, else
+   * MOE_LORA_ERR_UNSUPPORTED); 0: the row-major layouts.  Other values ->
+   * MOE_LORA_ERR_INVALID_ARGUMENT. */
+  int32_t packed_weights;
+  int32_t reserved[3];
 } moe_lora_options;
 
 /* Human-readable name of a status code (static storage). */
@@ -192,6 +197,24 @@ int moe_lora_forward(const moe_lora_dims *dims, const uint16_t *x, const uint16_
                      const moe_lora_adapters *lora, uint16_t *y_perm, void *ws, size_t ws_bytes,
                      moe_lora_stream_t main, moe_lora_stream_t side,
                      const moe_lora_options *opts);
+
+/* ---------------------------------------------------------------- pack weights
+ * Tile-packed copies of the expert weights for moe_lora_forward with
+ * opts->packed_weights = 1.  The grouped GEMMs read each expert's weights one 64-wide K
+ * step at a time for 128 output rows; the packed layout makes that piece one contiguous
+ * 16 KB block instead of 128 row segments 4 KB or more apart.  Layout of a weight with N
+ * rows and K columns per expert: blocks (e, t, s) in that order, t over the N / 128
+ * row tiles and s over the K / 64 column steps, each block the 128 x 64 sub-matrix
+ * row-major.  w_gate_up tiles are in the GEMM's gate/up pairing order: tile t holds the
+ * 64 gate rows of intermediate columns [64 t, 64 t + 64), then the 64 up rows of the
+ * same columns.  w_down tiles are rows [128 t, 128 t + 128) of [E, H, I].
+ *   w_gate_up [E, 2I, H] -> w_gate_up_packed (same size); w_down [E, H, I] ->
+ *   w_down_packed (same size).  Device pointers, 16-byte aligned, not overlapping.
+ * Requires hidden % 128 == 0 and inter % 64 == 0 (else MOE_LORA_ERR_UNSUPPORTED).
+ * A one-time transform, enqueued on `stream`; the library keeps no reference. */
+int moe_lora_pack_weights(const moe_lora_dims *dims, const uint16_t *w_gate_up, const uint16_t *w_down,
+                          uint16_t *w_gate_up_packed, uint16_t *w_down_packed,
+                          moe_lora_stream_t stream);
 
 /* ---------------------------------------------------------------- finalize
  * out[t, :] = bf16( sum_j topk_weights[t, j] * y_perm[expanded_to_permuted[t*k+j], :] ),

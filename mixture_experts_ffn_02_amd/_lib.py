@@ -36,6 +36,7 @@ EXPORTED = (
     "moe_lora_permute",
     "moe_lora_forward_workspace_size",
     "moe_lora_forward",
+    "moe_lora_pack_weights",
     "moe_lora_finalize",
 )
 
@@ -61,7 +62,7 @@ class Adapters(ctypes.Structure):
 class Options(ctypes.Structure):
     _fields_ = [("two_stream_max_tokens", c_int32), ("force_path", c_int32),
                 ("gate_up_event_begin", c_void_p), ("gate_up_event_end", c_void_p),
-                ("reserved", c_int32 * 4)]
+                ("packed_weights", c_int32), ("reserved", c_int32 * 3)]
 
 
 class MoELoRAError(RuntimeError):
@@ -104,6 +105,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_lora_forward.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, POINTER(Adapters), c_void_p, c_void_p,
                                      c_size_t, c_void_p, c_void_p, POINTER(Options)]
+    lib.moe_lora_pack_weights.restype = c_int
+    lib.moe_lora_pack_weights.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p]
     lib.moe_lora_finalize.restype = c_int
     lib.moe_lora_finalize.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p]

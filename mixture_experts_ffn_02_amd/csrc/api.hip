@@ -128,6 +128,24 @@ int moe_lora_permute(const moe_lora_dims *d, const uint16_t *x, const int32_t *p
                              reinterpret_cast<hipStream_t>(stream));
 }
 
+int moe_lora_pack_weights(const moe_lora_dims *d, const uint16_t *w_gate_up, const uint16_t *w_down,
+                          uint16_t *w_gate_up_packed, uint16_t *w_down_packed,
+                          moe_lora_stream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_LORA_OK) return st;
+  if (d->hidden % 128 != 0 || d->inter % 64 != 0) return MOE_LORA_ERR_UNSUPPORTED;
+  if (!w_gate_up || !w_down || !w_gate_up_packed || !w_down_packed || !aligned16(w_gate_up) ||
+      !aligned16(w_down) || !aligned16(w_gate_up_packed) || !aligned16(w_down_packed))
+    return MOE_LORA_ERR_INVALID_ARGUMENT;
+  const size_t n1 = (size_t)d->num_experts * 2 * d->inter * d->hidden, n2 = (size_t)d->num_experts * d->hidden * d->inter;
+  const uintptr_t a1 = reinterpret_cast<uintptr_t>(w_gate_up), b1 = reinterpret_cast<uintptr_t>(w_gate_up_packed);
+  const uintptr_t a2 = reinterpret_cast<uintptr_t>(w_down), b2 = reinterpret_cast<uintptr_t>(w_down_packed);
+  if ((a1 < b1 + 2 * n1 && b1 < a1 + 2 * n1) || (a2 < b2 + 2 * n2 && b2 < a2 + 2 * n2))
+    return MOE_LORA_ERR_INVALID_ARGUMENT;  // in-place packing is not supported
+  return moe::launch_pack_weights(*d, w_gate_up, w_down, w_gate_up_packed, w_down_packed,
+                                  reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t moe_lora_forward_workspace_size(const moe_lora_dims *d, const moe_lora_adapters *lora) {
   if (check_dims(d) != MOE_LORA_OK || check_lora_shape(lora) != MOE_LORA_OK) return 0;
   return moe::forward_workspace_size(*d, lora);
@@ -142,6 +160,9 @@ int moe_lora_forward(const moe_lora_dims *d, const uint16_t *x, const uint16_t *
   if (st != MOE_LORA_OK) return st;
   if ((st = check_lora(lora)) != MOE_LORA_OK) return st;
   if (opts && (opts->force_path < 0 || opts->force_path > 2)) return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (opts && opts->packed_weights != 0 && opts->packed_weights != 1) return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (opts && opts->packed_weights && (d->hidden % 128 != 0 || d->inter % 64 != 0))
+    return MOE_LORA_ERR_UNSUPPORTED;
   if (d->num_tokens == 0) return MOE_LORA_OK;
   if (!x && !x_perm) return MOE_LORA_ERR_INVALID_ARGUMENT;
   if ((x && !aligned16(x)) || (x_perm && !aligned16(x_perm))) return MOE_LORA_ERR_INVALID_ARGUMENT;

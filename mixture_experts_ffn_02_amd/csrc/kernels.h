@@ -35,6 +35,10 @@ int launch_permute(const uint16_t *x, const int32_t *p2e, uint16_t *x_perm, int 
 int launch_finalize(const uint16_t *y_perm, const float *w, const int32_t *e2p, uint16_t *out,
                     int T, int H, int K, hipStream_t s);
 
+// ---- tile-packed expert weights ---------------------------------------------------
+int launch_pack_weights(const moe_lora_dims &d, const uint16_t *w1, const uint16_t *w2, uint16_t *w1p,
+                        uint16_t *w2p, hipStream_t s);
+
 // ---- expert FFN (grouped GEMMs + LoRA) -----------------------------------------
 size_t forward_workspace_size(const moe_lora_dims &d, const moe_lora_adapters *lora);
 int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_perm,

@@ -81,6 +81,7 @@ struct GemmParams {
   float scaling[MOE_LORA_MAX_SLOTS];
   const uint16_t *lora_w[MOE_LORA_MAX_SLOTS];  // SHRINK: A [E, r, K]; ext: B [E, N, r]
   int lora_w_shared;  // lora_w holds one matrix per slot for all experts (shared-outer)
+  int w_packed;       // w is in the tile-packed layout (128-row x 64-column blocks)
   const float *part;                            // ext A source [splits][R][rmax]
   int part_splits;
   int rmax;
@@ -197,7 +198,11 @@ void moe_gemm_kernel(const GemmParams P) {
     L_end = min(total, (int)(blockIdx.x & 7) * per_xcd + per_xcd);
     L_step = (int)(gridDim.x >> 3);
   } else {
-    L = (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+    // On tile-packed weights the blocks take the tiles in launch order instead: with one
+    // tile per block the weight stream then runs through the packed buffer front to back
+    // (decode gate_up 151 -> 145 us; the XCD-grouped order is the faster one for the
+    // row-major layout, 6.5 against 6.1 TB/s in a streaming probe of the same pattern).
+    L = P.w_packed ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
     L_end = total;
     L_step = 0;
   }
@@ -259,6 +264,7 @@ void moe_gemm_kernel(const GemmParams P) {
     a_ptr[i] = (kHasMain && src >= 0) ? P.a + (size_t)src * P.K + (cc & 7) * 8 : nullptr;
   }
   int b_wrow[B_IT], b_lds[B_IT], b_c8[B_IT];
+  int b_pk[B_IT];  // tile-packed weights: offset of the chunk in its expert's block at K step 0
   bool b_has[B_IT];
 #pragma unroll
   for (int i = 0; i < B_IT; ++i) {
@@ -270,15 +276,19 @@ void moe_gemm_kernel(const GemmParams P) {
     b_lds[i] = lds_off(n, cc & 7);
     if (MODE == MODE_SHRINK) {
       b_wrow[i] = n;  // rank row, checked against the slot's rank
-    } else if (kGateUp) {
-      const int wnn = n / WTN, ccw = n % WTN;
-      const int half = ccw / (WTN / 2), j = ccw % (WTN / 2);
-      const int icol = col * (BN / 2) + wnn * (WTN / 2) + j;
-      b_wrow[i] = (icol < P.I) ? half * P.I + icol : -1;
+    } else if (kGateUp || MODE == MODE_GATEUP_F32) {
+      // gate/up row blocks (see brow()); the fp32 gate_up GEMM of the decomposed path keeps
+      // them too, so that both read the packed layout, and maps them back on its store
+      const int icol = col * (BN / 2) + (n / 128) * 64 + n % 64;
+      b_wrow[i] = (icol < P.I) ? ((n % 128) / 64) * P.I + icol : -1;
     } else {
       const int ng = col * BN + n;
       b_wrow[i] = (ng < P.N) ? ng : -1;
     }
+    // packed block (e, t, s) holds rows 128 t .. of the LDS order above for K step s
+    b_pk[i] = 0;
+    if constexpr (BN % 128 == 0)
+      b_pk[i] = ((col * (BN / 128) + n / 128) * (P.K / BK) * 128 + n % 128) * BK + (cc & 7) * 8;
   }
 
   u32x4_t ra[PF][A_IT], rb[PF][B_IT];
@@ -292,14 +302,21 @@ void moe_gemm_kernel(const GemmParams P) {
   };
 
   // full 64-wide K step, no predicates (see above)
+  // (pk: B from the tile-packed layout, where one K step of the tile is one contiguous
+  // 16 KB block per 128 rows)
   auto load_full = [&](int k0, const uint16_t *bbase, int bcount, u32x4_t(&xa)[A_IT],
-                       u32x4_t(&xb)[B_IT], auto nt) {
+                       u32x4_t(&xb)[B_IT], auto nt, auto pk) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) xa[i] = *reinterpret_cast<const u32x4_t *>(a_ptr[i] + k0);
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
-      const int wr = (b_wrow[i] >= 0 && b_wrow[i] < bcount) ? b_wrow[i] : 0;
-      const u32x4_t *src = reinterpret_cast<const u32x4_t *>(bbase + (size_t)wr * P.K + k0 + b_c8[i] * 8);
+      const u32x4_t *src;
+      if constexpr (decltype(pk)::value) {
+        src = reinterpret_cast<const u32x4_t *>(bbase + b_pk[i] + (size_t)(k0 / BK) * (128 * BK));
+      } else {
+        const int wr = (b_wrow[i] >= 0 && b_wrow[i] < bcount) ? b_wrow[i] : 0;
+        src = reinterpret_cast<const u32x4_t *>(bbase + (size_t)wr * P.K + k0 + b_c8[i] * 8);
+      }
       if constexpr (decltype(nt)::value)
         xb[i] = __builtin_nontemporal_load(src);
       else
@@ -335,6 +352,21 @@ void moe_gemm_kernel(const GemmParams P) {
 
   // Fragment rows are 16-aligned bases plus (lane & 15), so the swizzle depends on the lane
   // alone: one per-lane offset per 32-wide K chunk, everything else folds into immediates.
+  // First LDS row of B fragment fn of this wave.  gate_up tiles keep their B rows in blocks
+  // of 128, [64 gate rows | the 64 up rows of the same intermediate columns], so that a
+  // 128-row block is one tile of the packed weight layout; fragment fn < FN/2 is a gate
+  // fragment and fn + FN/2 the up fragment of the same 16 columns (SwiGLU pairs them in
+  // registers).  Other modes keep the natural order.
+  static_assert(!kGateUp || (BN % 128 == 0 && (WTN / 2) % 16 == 0), "gate_up tiles pair 64-row blocks");
+  static_assert(MODE != MODE_GATEUP_F32 || BN % 128 == 0, "gate_up tiles pair 64-row blocks");
+  auto brow = [&](int fn) -> int {
+    if constexpr (kGateUp) {
+      const int ic = wn * (WTN / 2) + (fn % (FN / 2)) * 16;
+      return (ic / 64) * 128 + (fn / (FN / 2)) * 64 + ic % 64;
+    } else {
+      return wn * WTN + fn * 16;
+    }
+  };
   int frag_lane[BK / 32];
 #pragma unroll
   for (int kk = 0; kk < BK / 32; ++kk) frag_lane[kk] = lds_off(lane & 15, kk * 4 + (lane >> 4));
@@ -348,7 +380,7 @@ void moe_gemm_kernel(const GemmParams P) {
         af[fm] = *reinterpret_cast<const u32x4_t *>(&As[buf][(wm * WTM + fm * 16) * BK + frag_lane[kk]]);
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        bfr[fn] = *reinterpret_cast<const u32x4_t *>(&Bs[buf][(wn * WTN + fn * 16) * BK + frag_lane[kk]]);
+        bfr[fn] = *reinterpret_cast<const u32x4_t *>(&Bs[buf][brow(fn) * BK + frag_lane[kk]]);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -400,7 +432,7 @@ void moe_gemm_kernel(const GemmParams P) {
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        bfr[fn] = *reinterpret_cast<const u32x4_t *>(&Bs[buf][(wn * WTN + fn * 16) * BK + frag_lane[kk]]);
+        bfr[fn] = *reinterpret_cast<const u32x4_t *>(&Bs[buf][brow(fn) * BK + frag_lane[kk]]);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -464,19 +496,19 @@ void moe_gemm_kernel(const GemmParams P) {
   // memory latency overlaps theirs); `tail_load(u)` runs at each of the last PF steps
   // before its compute, when register stage u has been stored and is free again.
   auto run_full = [&](int s_begin, int s_end, const uint16_t *bbase, int bcount, auto &&pre,
-                      auto &&tail_load, auto nt) {
+                      auto &&tail_load, auto nt, auto pk) {
     const int n = s_end - s_begin;
     const int n_main = (n / PF) * PF;
     if (n_main > 0) {
 #pragma unroll
-      for (int u = 0; u < PF; ++u) load_full((s_begin + u) * BK, bbase, bcount, ra[u], rb[u], nt);
+      for (int u = 0; u < PF; ++u) load_full((s_begin + u) * BK, bbase, bcount, ra[u], rb[u], nt, pk);
       pre();
       store_lds(0, ra[0], rb[0]);
       __syncthreads();
       for (int i = 0; i < n_main - PF; i += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-          load_full((s_begin + i + u + PF) * BK, bbase, bcount, ra[u], rb[u], nt);
+          load_full((s_begin + i + u + PF) * BK, bbase, bcount, ra[u], rb[u], nt, pk);
           compute(u & 1);
           store_lds((u + 1) & 1, ra[(u + 1) % PF], rb[(u + 1) % PF]);
           __syncthreads();
@@ -493,7 +525,7 @@ void moe_gemm_kernel(const GemmParams P) {
       pre();
     }
     for (int s = s_begin + n_main; s < s_end; ++s) {
-      load_full(s * BK, bbase, bcount, ra[0], rb[0], nt);
+      load_full(s * BK, bbase, bcount, ra[0], rb[0], nt, pk);
       store_lds(0, ra[0], rb[0]);
       __syncthreads();
       compute(0);
@@ -522,7 +554,7 @@ void moe_gemm_kernel(const GemmParams P) {
       const int r_a = P.rank[a];
       const uint16_t *bbase = P.lora_w[a] + (size_t)(P.lora_w_shared ? 0 : e) * r_a * P.K;
       zero_acc();
-      run_full(s0, s1f, bbase, r_a, [] {}, [](int) {}, std::false_type{});
+      run_full(s0, s1f, bbase, r_a, [] {}, [](int) {}, std::false_type{}, std::false_type{});
       if (s1 > s1f) run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
         load_tail(s1f * BK, bbase, r_a, xa, xb);
       });
@@ -649,10 +681,8 @@ void moe_gemm_kernel(const GemmParams P) {
           const int c8 = ((lane & 3) ^ ((n >> 2) & 3)) * 8;
           int wr;
           if (kGateUp) {
-            const int wnn = n / WTN, ccw = n % WTN;
-            const int half = ccw / (WTN / 2), j = ccw % (WTN / 2);
-            const int icol = col * (BN / 2) + wnn * (WTN / 2) + j;
-            wr = icol < P.I ? half * P.I + icol : 0;
+            const int icol = col * (BN / 2) + (n / 128) * 64 + n % 64;  // see brow()
+            wr = icol < P.I ? ((n % 128) / 64) * P.I + icol : 0;
           } else {
             const int ng = col * BN + n;
             wr = ng < P.N ? ng : 0;
@@ -667,26 +697,36 @@ void moe_gemm_kernel(const GemmParams P) {
       a2_copy();
       if (kHasExt && slot_mask) build_xs();  // visible after the main loop's first barrier
     };
-    auto main_loop = [&](auto nt) {
+    auto main_loop = [&](auto nt, auto pk) {
       if (kExtEarly && ext_early) {
         run_full(0, full, wbase, wcount, build, [&](int u) {
           load_ext_b_clamped(batch0[u] >= 0 ? batch0[u] : batch0[0], rb[u]);
-        }, nt);
+        }, nt, pk);
       } else {
-        run_full(0, full, wbase, wcount, build, [](int) {}, nt);
+        run_full(0, full, wbase, wcount, build, [](int) {}, nt, pk);
         if (full * BK < P.K) run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
           load_tail(full * BK, wbase, wcount, xa, xb);
         });
       }
     };
+    // the packed layout needs whole 128-row blocks and 64-wide K steps (checked by the host)
+    auto main_loop_pk = [&](auto nt) {
+      if constexpr (BN % 128 == 0) {
+        if (P.w_packed) {
+          main_loop(nt, std::true_type{});
+          return;
+        }
+      }
+      main_loop(nt, std::false_type{});
+    };
     if (kHasMain) {
       if constexpr (kStreamB) {
         if (single_mtile)
-          main_loop(std::true_type{});
+          main_loop_pk(std::true_type{});
         else
-          main_loop(std::false_type{});
+          main_loop_pk(std::false_type{});
       } else {
-        main_loop(std::false_type{});
+        main_loop_pk(std::false_type{});
       }
     } else {
       build();
@@ -702,7 +742,7 @@ void moe_gemm_kernel(const GemmParams P) {
         af[fm] = *reinterpret_cast<const u32x4_t *>(&Xs[(wm * WTM + fm * 16) * BK + frag_lane[0]]);
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int n = wn * WTN + fn * 16 + (lane & 15);
+        const int n = brow(fn) + (lane & 15);
         bfr[fn] = *reinterpret_cast<const u32x4_t *>(&Eb[n * kEbRank + (((lane >> 4) ^ ((n >> 2) & 3)) << 3)]);
       }
 #pragma unroll
@@ -880,7 +920,12 @@ void moe_gemm_kernel(const GemmParams P) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
-            const int n = col * BN + wn * WTN + fn * 16 + (lane & 15);
+            int n = col * BN + wn * WTN + fn * 16 + (lane & 15);
+            if constexpr (MODE == MODE_GATEUP_F32) {  // LDS row -> gate/up column
+              const int nl = wn * WTN + fn * 16 + (lane & 15);
+              const int icol = col * (BN / 2) + (nl / 128) * 64 + nl % 64;
+              n = icol < P.I ? ((nl % 128) / 64) * P.I + icol : P.N;
+            }
             if (r < rows && n < P.N) P.out_f32[(size_t)(row0 + r) * P.N + n] = acc[fm][fn][i];
           }
     }
@@ -1132,6 +1177,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->gate_up_event_begin) : nullptr;
   hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->gate_up_event_end) : nullptr;
   const int force = opts ? opts->force_path : 0;
+  const int packed = opts ? opts->packed_weights : 0;  // validated by the API layer
   int two_max = (opts && opts->two_stream_max_tokens > 0) ? opts->two_stream_max_tokens : kTwoStreamMaxT;
   if (two_max > kTwoStreamMaxT) two_max = kTwoStreamMaxT;
   const bool decomposed =
@@ -1158,6 +1204,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   gu.w = w1;
   gu.K = d.hidden;
   gu.N = 2 * d.inter;
+  gu.w_packed = packed;
 
   if (!decomposed) {
     // fused: shrink, then the GEMM appends the LoRA expand as extra K steps and applies
@@ -1235,6 +1282,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     P.w = w2;
     P.K = d.inter;
     P.N = d.hidden;
+    P.w_packed = packed;
     if (has_lora) {
       for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->b_down[s];
       P.lora_w_shared = lora->shared_outer;  // shared-outer: one B2 for all experts

@@ -14,7 +14,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import Adapters, Dims, Grouped, Options, check, load
+from ._lib import Adapters, Dims, Grouped, MoELoRAError, Options, check, load  # noqa: F401
 
 ROUTING_RENORMALIZE = _lib.ROUTING_RENORMALIZE
 ROUTING_DEEPSEEK_V3 = _lib.ROUTING_DEEPSEEK_V3
@@ -110,6 +110,13 @@ def moe_lora_forward(d: Dims, x, x_perm, expert_offsets, p2e, w_gate_up, w_down,
         ctypes.byref(opts) if opts is not None else None))
 
 
+def moe_lora_pack_weights(d: Dims, w_gate_up, w_down, w_gate_up_packed, w_down_packed,
+                          stream=None) -> None:
+    check("moe_lora_pack_weights", load().moe_lora_pack_weights(
+        ctypes.byref(d), _ptr(w_gate_up), _ptr(w_down), _ptr(w_gate_up_packed), _ptr(w_down_packed),
+        _stream(stream)))
+
+
 def moe_lora_finalize(d: Dims, y_perm, topk_weights, e2p, out, stream=None) -> None:
     check("moe_lora_finalize", load().moe_lora_finalize(
         ctypes.byref(d), _ptr(y_perm), _ptr(topk_weights), _ptr(e2p), _ptr(out), _stream(stream)))
@@ -128,16 +135,25 @@ class MoELoRALayer:
     """The routed MoE-LoRA layer on one GPU: route -> permute -> forward -> finalize.
 
     Buffers (routing outputs, workspaces, intermediates) are allocated once per token
-    count and reused, so repeated calls at one shape allocate nothing.
+    count and reused, so repeated calls at one shape allocate nothing.  With
+    packed_weights the layer keeps tile-packed copies of the expert weights (written once
+    by moe_lora_pack_weights) and runs the GEMMs on those; weights_prepacked says the
+    given weights already are in that layout.
     """
 
     def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int,
                  w_gate_up: torch.Tensor, w_down: torch.Tensor,
                  routing: int = ROUTING_RENORMALIZE, n_group: int = 1, topk_group: int = 1,
                  routed_scaling_factor: float = 1.0, correction_bias: Optional[torch.Tensor] = None,
-                 gather_on_load: bool = True):
+                 gather_on_load: bool = True, packed_weights: bool = False,
+                 weights_prepacked: bool = False):
         load()
         self.H, self.I, self.E, self.k = hidden, inter, num_experts, top_k
+        self.packed_weights = packed_weights or weights_prepacked
+        if packed_weights and not weights_prepacked:
+            w1p, w2p = torch.empty_like(w_gate_up), torch.empty_like(w_down)
+            moe_lora_pack_weights(self.dims(0), w_gate_up, w_down, w1p, w2p)
+            w_gate_up, w_down = w1p, w2p
         self.w_gate_up, self.w_down = w_gate_up, w_down
         self.routing = routing
         self.correction_bias = correction_bias
@@ -187,6 +203,12 @@ class MoELoRALayer:
                        self.routing, self.grouped, stream)
         if not self.gather_on_load:
             moe_lora_permute(d, x, b["p2e"], b["x_perm"], stream)
+        if self.packed_weights:
+            o = Options()
+            if opts is not None:
+                ctypes.memmove(ctypes.byref(o), ctypes.byref(opts), ctypes.sizeof(Options))
+            o.packed_weights = 1
+            opts = o
         moe_lora_forward(d, x, b["x_perm"], b["off"], b["p2e"], self.w_gate_up, self.w_down,
                          c_lora, b["y"], b["fws"], stream, side_stream, opts)
         moe_lora_finalize(d, b["y"], b["w"], b["e2p"], b["out"], stream)

@@ -152,6 +152,15 @@ def test_forward_argument_checks():
     o.force_path = -1
     assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
                                 None, ctypes.byref(o)) == _lib.ERR_INVALID_ARGUMENT
+    # packed_weights is a flag, and needs hidden % 128 == 0, inter % 64 == 0
+    o = _lib.Options()
+    o.packed_weights = 2
+    assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
+                                None, ctypes.byref(o)) == _lib.ERR_INVALID_ARGUMENT
+    o.packed_weights = 1
+    d_odd = _lib.Dims(4, 200, 88, 8, 2)
+    assert lib.moe_lora_forward(ctypes.byref(d_odd), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30,
+                                None, None, ctypes.byref(o)) == _lib.ERR_UNSUPPORTED
     # shared_outer is a flag
     a.shared_outer = 2
     assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
@@ -169,3 +178,14 @@ def test_empty_batch_is_a_noop_without_device_work():
     assert lib.moe_lora_finalize(ctypes.byref(d), None, None, None, None, None) == _lib.OK
     assert lib.moe_lora_forward(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
                                 0, None, None, None) == _lib.OK
+
+
+def test_pack_weights_argument_checks():
+    lib = pkg.load()
+    d = _lib.Dims(4, 256, 128, 8, 2)
+    other = FAKE + (1 << 24)
+    assert lib.moe_lora_pack_weights(ctypes.byref(_lib.Dims(4, 200, 88, 8, 2)), FAKE, FAKE, other, other,
+                                     None) == _lib.ERR_UNSUPPORTED
+    assert lib.moe_lora_pack_weights(ctypes.byref(d), None, FAKE, other, other, None) == _lib.ERR_INVALID_ARGUMENT
+    # packing in place (overlapping source and destination) is rejected
+    assert lib.moe_lora_pack_weights(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID_ARGUMENT

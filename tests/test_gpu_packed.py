@@ -1,0 +1,88 @@
+"""Tile-packed expert weights (moe_lora_pack_weights + packed_weights).
+
+The pack is checked against the documented layout unpacked on the host with numpy, and
+the layer on packed weights must be bit-identical to the layer on the row-major weights
+(same kernels, same arithmetic; only the addresses of the weight loads change) on every
+tile shape: 16-row decode tiles, 64-row tiles, 128 x 256 prefill tiles (two packed tiles
+per B tile), with and without LoRA, and on the two-stream path.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import GpuLayer, dev, say
+from mixture_experts_ffn_02_amd import moe_lora as ml
+from synth import NAMED_CONFIGS, Workload, make_config
+from test_gpu_parity import RAGGED
+
+pytestmark = pytest.mark.gpu
+
+DSV3_SMALL = make_config(name="dsv3_shape_T256_H7168_I2048_E16_k8_r32", cfg_id=204, T=256, H=7168, I=2048,
+                         E=16, top_k=8, routing="deepseek_v3", n_group=8, topk_group=4,
+                         routed_scaling_factor=2.5, corr_bias_std=0.1, w_std=0.01, lora_a_std=0.01,
+                         lora_b_std=0.01, slots=((32, 1.0),))
+PREFILL_SMALL = make_config(name="prefill_shape_T2048_H2048_I768_E16_k8_r16", cfg_id=205, T=2048, H=2048,
+                            I=768, E=16, top_k=8, logit_offset_std=0.5, slots=((16, 2.0),))
+
+
+def _unpack(packed: np.ndarray, E: int, N: int, K: int, I_gate_up: int = 0) -> np.ndarray:
+    """Row-major [E, N, K] from the packed layout: blocks (e, t, s) of 128 x 64."""
+    blocks = packed.reshape(E, N // 128, K // 64, 128, 64)
+    tiles = blocks.transpose(0, 1, 3, 2, 4).reshape(E, N // 128, 128, K)  # [e, t, r, k]
+    out = np.empty((E, N, K), dtype=packed.dtype)
+    if I_gate_up:
+        for t in range(N // 128):
+            out[:, t * 64:(t + 1) * 64] = tiles[:, t, :64]
+            out[:, I_gate_up + t * 64:I_gate_up + (t + 1) * 64] = tiles[:, t, 64:]
+    else:
+        out[:] = tiles.reshape(E, N, K)
+    return out
+
+
+def test_pack_matches_the_documented_layout():
+    cfg = NAMED_CONFIGS[1]
+    g = GpuLayer(Workload(cfg, 0))
+    d = ml.Dims(0, cfg.H, cfg.I, cfg.E, cfg.top_k)
+    w1p, w2p = torch.empty_like(g.w1), torch.empty_like(g.w2)
+    ml.moe_lora_pack_weights(d, g.w1, g.w2, w1p, w2p)
+    torch.cuda.synchronize()
+    u1 = _unpack(w1p.cpu().numpy(), cfg.E, 2 * cfg.I, cfg.H, cfg.I)
+    u2 = _unpack(w2p.cpu().numpy(), cfg.E, cfg.H, cfg.I)
+    np.testing.assert_array_equal(u1, g.w1.cpu().numpy())
+    np.testing.assert_array_equal(u2, g.w2.cpu().numpy())
+    # spot check: block (e, t, s), row r, column k of the gate_up pack is gate row 64 t + r
+    e, t, s, r, k = 3, 1, 2, 5, 7
+    blk = ((e * (2 * cfg.I // 128) + t) * (cfg.H // 64) + s) * 128 * 64
+    assert w1p.view(-1)[blk + r * 64 + k].item() == g.w1[e, 64 * t + r, 64 * s + k].item()
+
+
+@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], NAMED_CONFIGS[4], DSV3_SMALL,
+                                 PREFILL_SMALL], ids=lambda c: c.name)
+def test_packed_weights_bit_identical(cfg):
+    say(f"[packed] {cfg.name}")
+    g = GpuLayer(Workload(cfg, 0), stream_weights=True)
+    c = g.cfg
+    layer = g.layer()
+    packed = ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, g.w1, g.w2, g.routing, c.n_group, c.topk_group,
+                             c.routed_scaling_factor, g.bias, packed_weights=True)
+    lora = g.lora_slots()
+    for lr in (lora, None):
+        a = layer(g.x, g.logits, lr).clone()
+        b = packed(g.x, g.logits, lr).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"lora={lr is not None}"
+    if c.T <= 256:  # the two-stream path (its fp32 gate_up GEMM reads the packed weights too)
+        side = torch.cuda.Stream()
+        a = layer(g.x, g.logits, lora, side_stream=side).clone()
+        b = packed(g.x, g.logits, lora, side_stream=side).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_packed_weights_need_whole_tiles():
+    g = GpuLayer(Workload(RAGGED, 0))
+    c = g.cfg
+    with pytest.raises(ml.MoELoRAError):
+        ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, g.w1, g.w2, packed_weights=True)
+    torch.cuda.synchronize()
