@@ -43,8 +43,10 @@ def parse():
     ap.add_argument("--only-lora-on", action="store_true",
                     help="run only the LoRA-on leg (for counter collection)")
     ap.add_argument("--quiet", action="store_true")
-    ap.add_argument("--weights", choices=("packed", "row-major"), default="packed",
-                    help="expert weight layout the GEMMs read (packed once before timing)")
+    ap.add_argument("--weights", choices=("packed-gate-up", "packed", "row-major"),
+                    default="packed-gate-up",
+                    help="expert weight layout the GEMMs read: the gate_up weights (or both) "
+                         "tile-packed once before timing, or both row-major")
     return ap.parse_args()
 
 
@@ -153,7 +155,8 @@ def main():
     w2 = stack_to_device("w_down", (cfg.H, cfg.I))
     lora_t = [{k: t16(v) for k, v in wl.lora_all(a).items()} for a in range(cfg.num_slots)]
     routing = ml.ROUTING_DEEPSEEK_V3 if cfg.routing == "deepseek_v3" else ml.ROUTING_RENORMALIZE
-    packed = args.weights == "packed"
+    packed = {"packed-gate-up": ml.PACKED_GATE_UP, "packed": ml.PACKED_GATE_UP | ml.PACKED_DOWN,
+              "row-major": 0}[args.weights]
     layer = ml.MoELoRALayer(cfg.H, cfg.I, cfg.E, cfg.top_k, w1, w2, routing, cfg.n_group,
                             cfg.topk_group, cfg.routed_scaling_factor, bias, gather_on_load=True,
                             packed_weights=packed)
@@ -312,7 +315,9 @@ def main():
         "data": "synthetic (seeded N(0,sigma) bf16 tensors of the workload's shapes; no checkpoint)",
         "config": {"workload": cfg.name, **cfg.describe(), "parallelism": "single GPU",
                    "permute": "gathered inside the GEMM and shrink loads",
-                   "weights": "tile-packed once before timing" if packed else "row-major"},
+                   "weights": {"packed-gate-up": "gate_up tile-packed once before timing, down row-major",
+                               "packed": "tile-packed once before timing",
+                               "row-major": "row-major"}[args.weights]},
         "lora_off_value": round(tok_off, 1),
         "lora_ratio": round(tok_on / tok_off, 4),
         "ms_per_step_lora_off": round(t_off * 1e3, 4),

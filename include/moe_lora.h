@@ -116,10 +116,10 @@ typedef struct {
    * after the gate_up GEMM launch, so a caller can time that kernel alone. */
   void *gate_up_event_begin;
   void *gate_up_event_end;
-  /* 1: w_gate_up and w_down are the tile-packed copies written by
-   * moe_lora_pack_weights (hidden % 128 == 0 and inter % 64 == 0, else
-   * MOE_LORA_ERR_UNSUPPORTED); 0: the row-major layouts.  Other values ->
-   * MOE_LORA_ERR_INVALID_ARGUMENT. */
+  /* Which weights are the tile-packed copies written by moe_lora_pack_weights: bit 0
+   * w_gate_up, bit 1 w_down (0 = both row-major).  Any packed weight needs
+   * hidden % 128 == 0 and inter % 64 == 0 (else MOE_LORA_ERR_UNSUPPORTED); values
+   * outside 0..3 -> MOE_LORA_ERR_INVALID_ARGUMENT. */
   int32_t packed_weights;
   int32_t reserved[3];
 } moe_lora_options;
@@ -209,7 +209,8 @@ int moe_lora_forward(const moe_lora_dims *dims, const uint16_t *x, const uint16_
  * 64 gate rows of intermediate columns [64 t, 64 t + 64), then the 64 up rows of the
  * same columns.  w_down tiles are rows [128 t, 128 t + 128) of [E, H, I].
  *   w_gate_up [E, 2I, H] -> w_gate_up_packed (same size); w_down [E, H, I] ->
- *   w_down_packed (same size).  Device pointers, 16-byte aligned, not overlapping.
+ *   w_down_packed (same size).  Device pointers, 16-byte aligned, not overlapping; a
+ *   pair given as two NULLs is skipped (at least one pair is needed).
  * Requires hidden % 128 == 0 and inter % 64 == 0 (else MOE_LORA_ERR_UNSUPPORTED).
  * A one-time transform, enqueued on `stream`; the library keeps no reference. */
 int moe_lora_pack_weights(const moe_lora_dims *dims, const uint16_t *w_gate_up, const uint16_t *w_down,

@@ -134,13 +134,16 @@ int moe_lora_pack_weights(const moe_lora_dims *d, const uint16_t *w_gate_up, con
   int st = check_dims(d);
   if (st != MOE_LORA_OK) return st;
   if (d->hidden % 128 != 0 || d->inter % 64 != 0) return MOE_LORA_ERR_UNSUPPORTED;
-  if (!w_gate_up || !w_down || !w_gate_up_packed || !w_down_packed || !aligned16(w_gate_up) ||
-      !aligned16(w_down) || !aligned16(w_gate_up_packed) || !aligned16(w_down_packed))
+  const bool do1 = w_gate_up || w_gate_up_packed, do2 = w_down || w_down_packed;
+  if (!do1 && !do2) return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (do1 && (!w_gate_up || !w_gate_up_packed || !aligned16(w_gate_up) || !aligned16(w_gate_up_packed)))
+    return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (do2 && (!w_down || !w_down_packed || !aligned16(w_down) || !aligned16(w_down_packed)))
     return MOE_LORA_ERR_INVALID_ARGUMENT;
   const size_t n1 = (size_t)d->num_experts * 2 * d->inter * d->hidden, n2 = (size_t)d->num_experts * d->hidden * d->inter;
   const uintptr_t a1 = reinterpret_cast<uintptr_t>(w_gate_up), b1 = reinterpret_cast<uintptr_t>(w_gate_up_packed);
   const uintptr_t a2 = reinterpret_cast<uintptr_t>(w_down), b2 = reinterpret_cast<uintptr_t>(w_down_packed);
-  if ((a1 < b1 + 2 * n1 && b1 < a1 + 2 * n1) || (a2 < b2 + 2 * n2 && b2 < a2 + 2 * n2))
+  if ((do1 && a1 < b1 + 2 * n1 && b1 < a1 + 2 * n1) || (do2 && a2 < b2 + 2 * n2 && b2 < a2 + 2 * n2))
     return MOE_LORA_ERR_INVALID_ARGUMENT;  // in-place packing is not supported
   return moe::launch_pack_weights(*d, w_gate_up, w_down, w_gate_up_packed, w_down_packed,
                                   reinterpret_cast<hipStream_t>(stream));
@@ -160,7 +163,7 @@ int moe_lora_forward(const moe_lora_dims *d, const uint16_t *x, const uint16_t *
   if (st != MOE_LORA_OK) return st;
   if ((st = check_lora(lora)) != MOE_LORA_OK) return st;
   if (opts && (opts->force_path < 0 || opts->force_path > 2)) return MOE_LORA_ERR_INVALID_ARGUMENT;
-  if (opts && opts->packed_weights != 0 && opts->packed_weights != 1) return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (opts && (opts->packed_weights < 0 || opts->packed_weights > 3)) return MOE_LORA_ERR_INVALID_ARGUMENT;
   if (opts && opts->packed_weights && (d->hidden % 128 != 0 || d->inter % 64 != 0))
     return MOE_LORA_ERR_UNSUPPORTED;
   if (d->num_tokens == 0) return MOE_LORA_OK;

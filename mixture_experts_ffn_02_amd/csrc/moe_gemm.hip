@@ -1177,7 +1177,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->gate_up_event_begin) : nullptr;
   hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->gate_up_event_end) : nullptr;
   const int force = opts ? opts->force_path : 0;
-  const int packed = opts ? opts->packed_weights : 0;  // validated by the API layer
+  const int packed = opts ? opts->packed_weights : 0;  // bit 0 W1, bit 1 W2 (validated by the API)
   int two_max = (opts && opts->two_stream_max_tokens > 0) ? opts->two_stream_max_tokens : kTwoStreamMaxT;
   if (two_max > kTwoStreamMaxT) two_max = kTwoStreamMaxT;
   const bool decomposed =
@@ -1204,7 +1204,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   gu.w = w1;
   gu.K = d.hidden;
   gu.N = 2 * d.inter;
-  gu.w_packed = packed;
+  gu.w_packed = packed & 1;
 
   if (!decomposed) {
     // fused: shrink, then the GEMM appends the LoRA expand as extra K steps and applies
@@ -1282,7 +1282,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     P.w = w2;
     P.K = d.inter;
     P.N = d.hidden;
-    P.w_packed = packed;
+    P.w_packed = (packed >> 1) & 1;
     if (has_lora) {
       for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->b_down[s];
       P.lora_w_shared = lora->shared_outer;  // shared-outer: one B2 for all experts

@@ -52,9 +52,11 @@ int launch_pack(const uint16_t *src, uint16_t *dst, int E, int N, int K, int I_g
 
 int launch_pack_weights(const moe_lora_dims &d, const uint16_t *w1, const uint16_t *w2, uint16_t *w1p,
                         uint16_t *w2p, hipStream_t s) {
-  int st = launch_pack(w1, w1p, d.num_experts, 2 * d.inter, d.hidden, d.inter, s);
-  if (st != ST_OK) return st;
-  return launch_pack(w2, w2p, d.num_experts, d.hidden, d.inter, 0, s);
+  if (w1) {
+    const int st = launch_pack(w1, w1p, d.num_experts, 2 * d.inter, d.hidden, d.inter, s);
+    if (st != ST_OK) return st;
+  }
+  return w2 ? launch_pack(w2, w2p, d.num_experts, d.hidden, d.inter, 0, s) : ST_OK;
 }
 
 }  // namespace moe

@@ -18,6 +18,9 @@ from ._lib import Adapters, Dims, Grouped, MoELoRAError, Options, check, load  #
 
 ROUTING_RENORMALIZE = _lib.ROUTING_RENORMALIZE
 ROUTING_DEEPSEEK_V3 = _lib.ROUTING_DEEPSEEK_V3
+# moe_lora_options.packed_weights bits
+PACKED_GATE_UP = 1
+PACKED_DOWN = 2
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -135,25 +138,34 @@ class MoELoRALayer:
     """The routed MoE-LoRA layer on one GPU: route -> permute -> forward -> finalize.
 
     Buffers (routing outputs, workspaces, intermediates) are allocated once per token
-    count and reused, so repeated calls at one shape allocate nothing.  With
-    packed_weights the layer keeps tile-packed copies of the expert weights (written once
-    by moe_lora_pack_weights) and runs the GEMMs on those; weights_prepacked says the
-    given weights already are in that layout.
+    count and reused, so repeated calls at one shape allocate nothing.  packed_weights
+    (PACKED_GATE_UP | PACKED_DOWN bits; True = both) makes the layer keep tile-packed
+    copies of those expert weights (written once by moe_lora_pack_weights) and run the
+    GEMMs on them; weights_prepacked gives the bits of the weights that are passed in
+    already packed.
     """
 
     def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int,
                  w_gate_up: torch.Tensor, w_down: torch.Tensor,
                  routing: int = ROUTING_RENORMALIZE, n_group: int = 1, topk_group: int = 1,
                  routed_scaling_factor: float = 1.0, correction_bias: Optional[torch.Tensor] = None,
-                 gather_on_load: bool = True, packed_weights: bool = False,
-                 weights_prepacked: bool = False):
+                 gather_on_load: bool = True, packed_weights=0, weights_prepacked=0):
         load()
         self.H, self.I, self.E, self.k = hidden, inter, num_experts, top_k
-        self.packed_weights = packed_weights or weights_prepacked
-        if packed_weights and not weights_prepacked:
-            w1p, w2p = torch.empty_like(w_gate_up), torch.empty_like(w_down)
-            moe_lora_pack_weights(self.dims(0), w_gate_up, w_down, w1p, w2p)
-            w_gate_up, w_down = w1p, w2p
+        both = PACKED_GATE_UP | PACKED_DOWN
+        to_pack = both if packed_weights is True else int(packed_weights)
+        pre = both if weights_prepacked is True else int(weights_prepacked)
+        if (to_pack | pre) & ~both:
+            raise ValueError("packed_weights / weights_prepacked take PACKED_GATE_UP | PACKED_DOWN bits")
+        to_pack &= ~pre
+        if to_pack:
+            w1p = torch.empty_like(w_gate_up) if to_pack & PACKED_GATE_UP else None
+            w2p = torch.empty_like(w_down) if to_pack & PACKED_DOWN else None
+            moe_lora_pack_weights(self.dims(0), w_gate_up if w1p is not None else None,
+                                  w_down if w2p is not None else None, w1p, w2p)
+            w_gate_up = w1p if w1p is not None else w_gate_up
+            w_down = w2p if w2p is not None else w_down
+        self.packed_weights = to_pack | pre
         self.w_gate_up, self.w_down = w_gate_up, w_down
         self.routing = routing
         self.correction_bias = correction_bias
@@ -207,7 +219,7 @@ class MoELoRALayer:
             o = Options()
             if opts is not None:
                 ctypes.memmove(ctypes.byref(o), ctypes.byref(opts), ctypes.sizeof(Options))
-            o.packed_weights = 1
+            o.packed_weights = self.packed_weights
             opts = o
         moe_lora_forward(d, x, b["x_perm"], b["off"], b["p2e"], self.w_gate_up, self.w_down,
                          c_lora, b["y"], b["fws"], stream, side_stream, opts)

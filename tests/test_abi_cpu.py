@@ -152,9 +152,9 @@ def test_forward_argument_checks():
     o.force_path = -1
     assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
                                 None, ctypes.byref(o)) == _lib.ERR_INVALID_ARGUMENT
-    # packed_weights is a flag, and needs hidden % 128 == 0, inter % 64 == 0
+    # packed_weights holds two bits, and a packed weight needs hidden % 128 == 0, inter % 64 == 0
     o = _lib.Options()
-    o.packed_weights = 2
+    o.packed_weights = 4
     assert lib.moe_lora_forward(ctypes.byref(d), *args, ctypes.byref(a), FAKE, FAKE, 1 << 30, None,
                                 None, ctypes.byref(o)) == _lib.ERR_INVALID_ARGUMENT
     o.packed_weights = 1
@@ -187,5 +187,6 @@ def test_pack_weights_argument_checks():
     assert lib.moe_lora_pack_weights(ctypes.byref(_lib.Dims(4, 200, 88, 8, 2)), FAKE, FAKE, other, other,
                                      None) == _lib.ERR_UNSUPPORTED
     assert lib.moe_lora_pack_weights(ctypes.byref(d), None, FAKE, other, other, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.moe_lora_pack_weights(ctypes.byref(d), None, None, None, None, None) == _lib.ERR_INVALID_ARGUMENT
     # packing in place (overlapping source and destination) is rejected
     assert lib.moe_lora_pack_weights(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID_ARGUMENT

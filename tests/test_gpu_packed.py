@@ -57,15 +57,21 @@ def test_pack_matches_the_documented_layout():
     assert w1p.view(-1)[blk + r * 64 + k].item() == g.w1[e, 64 * t + r, 64 * s + k].item()
 
 
-@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], NAMED_CONFIGS[4], DSV3_SMALL,
-                                 PREFILL_SMALL], ids=lambda c: c.name)
-def test_packed_weights_bit_identical(cfg):
-    say(f"[packed] {cfg.name}")
+BOTH = ml.PACKED_GATE_UP | ml.PACKED_DOWN
+
+
+@pytest.mark.parametrize("cfg,mask", [(NAMED_CONFIGS[1], BOTH), (NAMED_CONFIGS[2], BOTH),
+                                      (NAMED_CONFIGS[2], ml.PACKED_GATE_UP), (NAMED_CONFIGS[2], ml.PACKED_DOWN),
+                                      (NAMED_CONFIGS[4], BOTH), (DSV3_SMALL, BOTH), (PREFILL_SMALL, BOTH),
+                                      (PREFILL_SMALL, ml.PACKED_GATE_UP)],
+                         ids=lambda v: v.name if hasattr(v, "name") else f"mask{v}")
+def test_packed_weights_bit_identical(cfg, mask):
+    say(f"[packed] {cfg.name} mask={mask}")
     g = GpuLayer(Workload(cfg, 0), stream_weights=True)
     c = g.cfg
     layer = g.layer()
     packed = ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, g.w1, g.w2, g.routing, c.n_group, c.topk_group,
-                             c.routed_scaling_factor, g.bias, packed_weights=True)
+                             c.routed_scaling_factor, g.bias, packed_weights=mask)
     lora = g.lora_slots()
     for lr in (lora, None):
         a = layer(g.x, g.logits, lr).clone()
