@@ -44,7 +44,7 @@ def parse():
                     help="run only the LoRA-on leg (for counter collection)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--weights", choices=("packed-gate-up", "packed", "row-major"),
-                    default="packed-gate-up",
+                    default="packed",
                     help="expert weight layout the GEMMs read: the gate_up weights (or both) "
                          "tile-packed once before timing, or both row-major")
     return ap.parse_args()

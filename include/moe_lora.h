@@ -203,8 +203,8 @@ int moe_lora_forward(const moe_lora_dims *dims, const uint16_t *x, const uint16_
  * opts->packed_weights = 1.  The grouped GEMMs read each expert's weights one 64-wide K
  * step at a time for 128 output rows; the packed layout makes that piece one contiguous
  * 16 KB block instead of 128 row segments 4 KB or more apart.  Layout of a weight with N
- * rows and K columns per expert: blocks (e, t, s) in that order, t over the N / 128
- * row tiles and s over the K / 64 column steps, each block the 128 x 64 sub-matrix
+ * rows and K columns per expert: blocks (e, s, t) in that order, s over the K / 64
+ * column steps and t over the N / 128 row tiles, each block the 128 x 64 sub-matrix
  * row-major.  w_gate_up tiles are in the GEMM's gate/up pairing order: tile t holds the
  * 64 gate rows of intermediate columns [64 t, 64 t + 64), then the 64 up rows of the
  * same columns.  w_down tiles are rows [128 t, 128 t + 128) of [E, H, I].

@@ -285,10 +285,9 @@ void moe_gemm_kernel(const GemmParams P) {
       const int ng = col * BN + n;
       b_wrow[i] = (ng < P.N) ? ng : -1;
     }
-    // packed block (e, t, s) holds rows 128 t .. of the LDS order above for K step s
+    // packed block (e, s, t) holds rows 128 t .. of the LDS order above for K step s
     b_pk[i] = 0;
-    if constexpr (BN % 128 == 0)
-      b_pk[i] = ((col * (BN / 128) + n / 128) * (P.K / BK) * 128 + n % 128) * BK + (cc & 7) * 8;
+    if constexpr (BN % 128 == 0) b_pk[i] = ((col * (BN / 128) + n / 128) * 128 + n % 128) * BK + (cc & 7) * 8;
   }
 
   u32x4_t ra[PF][A_IT], rb[PF][B_IT];
@@ -302,8 +301,8 @@ void moe_gemm_kernel(const GemmParams P) {
   };
 
   // full 64-wide K step, no predicates (see above)
-  // (pk: B from the tile-packed layout, where one K step of the tile is one contiguous
-  // 16 KB block per 128 rows)
+  // (pk: B from the tile-packed layout, where one K step of 128 rows is one contiguous
+  // 16 KB block and the blocks of one K step are adjacent)
   auto load_full = [&](int k0, const uint16_t *bbase, int bcount, u32x4_t(&xa)[A_IT],
                        u32x4_t(&xb)[B_IT], auto nt, auto pk) {
 #pragma unroll
@@ -312,7 +311,7 @@ void moe_gemm_kernel(const GemmParams P) {
     for (int i = 0; i < B_IT; ++i) {
       const u32x4_t *src;
       if constexpr (decltype(pk)::value) {
-        src = reinterpret_cast<const u32x4_t *>(bbase + b_pk[i] + (size_t)(k0 / BK) * (128 * BK));
+        src = reinterpret_cast<const u32x4_t *>(bbase + b_pk[i] + (size_t)(k0 / BK) * P.N * BK);
       } else {
         const int wr = (b_wrow[i] >= 0 && b_wrow[i] < bcount) ? b_wrow[i] : 0;
         src = reinterpret_cast<const u32x4_t *>(bbase + (size_t)wr * P.K + k0 + b_c8[i] * 8);

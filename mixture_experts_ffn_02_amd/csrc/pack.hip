@@ -6,9 +6,10 @@
 // 4 KB or more apart; in the packed layout it is one contiguous 16 KB block, which a
 // streaming probe on MI355X reads at 7.1 TB/s against 6.2 TB/s for the scattered form.
 //
-// Packed layout of a weight with N rows and K columns per expert: blocks (e, t, s) in
-// that order, t over 128-row tiles and s over 64-wide K steps, each block the 128 x 64
-// sub-matrix row-major.  The gate_up tiles are in the GEMM's pairing order: tile t holds
+// Packed layout of a weight with N rows and K columns per expert: blocks (e, s, t) in
+// that order, s over 64-wide K steps and t over 128-row tiles, each block the 128 x 64
+// sub-matrix row-major.  Blocks that GEMM tiles running side by side read at the same
+// K step are neighbours (one contiguous stream, and no L2 set aliasing between them).  The gate_up tiles are in the GEMM's pairing order: tile t holds
 // the 64 gate rows of intermediate columns [64 t, 64 t + 64) and then the 64 up rows of
 // the same columns.
 #include "common.h"
@@ -27,9 +28,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
   if (q >= total) return;
   const int c8 = (int)(q & 7);             // chunk of the 64-wide row piece
   const int r = (int)((q >> 3) & 127);     // row inside the tile
-  const long long blk = q >> 10;           // (e, t, s) block
-  const int s = (int)(blk % ksteps);
-  const int t = (int)((blk / ksteps) % tiles);
+  const long long blk = q >> 10;           // (e, s, t) block
+  const int t = (int)(blk % tiles);
+  const int s = (int)((blk / tiles) % ksteps);
   const int e = (int)(blk / ((long long)ksteps * tiles));
   int row;
   if (I_gate_up > 0) row = (r / 64) * I_gate_up + t * 64 + r % 64;  // gate rows, then up rows

@@ -27,9 +27,9 @@ PREFILL_SMALL = make_config(name="prefill_shape_T2048_H2048_I768_E16_k8_r16", cf
 
 
 def _unpack(packed: np.ndarray, E: int, N: int, K: int, I_gate_up: int = 0) -> np.ndarray:
-    """Row-major [E, N, K] from the packed layout: blocks (e, t, s) of 128 x 64."""
-    blocks = packed.reshape(E, N // 128, K // 64, 128, 64)
-    tiles = blocks.transpose(0, 1, 3, 2, 4).reshape(E, N // 128, 128, K)  # [e, t, r, k]
+    """Row-major [E, N, K] from the packed layout: blocks (e, s, t) of 128 x 64."""
+    blocks = packed.reshape(E, K // 64, N // 128, 128, 64)
+    tiles = blocks.transpose(0, 2, 3, 1, 4).reshape(E, N // 128, 128, K)  # [e, t, r, k]
     out = np.empty((E, N, K), dtype=packed.dtype)
     if I_gate_up:
         for t in range(N // 128):
@@ -51,9 +51,9 @@ def test_pack_matches_the_documented_layout():
     u2 = _unpack(w2p.cpu().numpy(), cfg.E, cfg.H, cfg.I)
     np.testing.assert_array_equal(u1, g.w1.cpu().numpy())
     np.testing.assert_array_equal(u2, g.w2.cpu().numpy())
-    # spot check: block (e, t, s), row r, column k of the gate_up pack is gate row 64 t + r
+    # spot check: block (e, s, t), row r, column k of the gate_up pack is gate row 64 t + r
     e, t, s, r, k = 3, 1, 2, 5, 7
-    blk = ((e * (2 * cfg.I // 128) + t) * (cfg.H // 64) + s) * 128 * 64
+    blk = ((e * (cfg.H // 64) + s) * (2 * cfg.I // 128) + t) * 128 * 64
     assert w1p.view(-1)[blk + r * 64 + k].item() == g.w1[e, 64 * t + r, 64 * s + k].item()
 
 
