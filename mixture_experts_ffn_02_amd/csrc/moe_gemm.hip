@@ -97,10 +97,12 @@ struct GemmParams {
   const int32_t *row_slot;
 };
 
-// Register budget: decode-height tiles keep three waves per SIMD (the LDS allows three
-// blocks per CU); taller tiles two.
+// Register budget: two waves per SIMD (256 VGPRs) for every tile height.  Three waves on
+// the 16-row tiles would fit the LDS but cap them at 168 VGPRs, where the four register
+// stages and the LoRA code spill to scratch on every tile (decode gate_up 155 -> 131 us
+// without the cap).
 template <int BM, int BN, int WM, int WN, int MODE, int PF>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(BM <= 32 ? 3 : 2)))
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void moe_gemm_kernel(const GemmParams P) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
