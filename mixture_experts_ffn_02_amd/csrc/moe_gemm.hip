@@ -129,6 +129,10 @@ void moe_gemm_kernel(const GemmParams P) {
   __shared__ int s_mask[2];  // slots present in the tile, by tile parity
   __shared__ int s_off[MOE_LORA_MAX_EXPERTS + 1];   // expert_offsets
   __shared__ int s_tpre[MOE_LORA_MAX_EXPERTS + 1];  // first m-tile index of each expert
+  // rank of each slot, for code that looks it up by a row's slot (P.rank[a] with a
+  // per-lane a is a vector load from the argument block, which waits behind the weight
+  // stream)
+  __shared__ int s_rank[MOE_LORA_MAX_SLOTS];
   // LoRA expand A operand of the tile: row r holds bf16(s_a * sum of shrink partials) over
   // the rank columns of its own slot (zero elsewhere); built once, masked per slot later
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kHasExt ? BM * BK : 8];
@@ -160,6 +164,9 @@ void moe_gemm_kernel(const GemmParams P) {
   // LDS.  Tall tiles (prefill) run persistent blocks that loop over tiles; decode-height
   // tiles take one tile per block.  The hardware places block b on XCD b % 8.
   for (int i = tid; i <= P.E; i += NT) s_off[i] = P.offsets[i];
+#pragma unroll
+  for (int s2 = 0; s2 < MOE_LORA_MAX_SLOTS; ++s2)
+    if (tid == s2) s_rank[s2] = P.rank[s2];
   __syncthreads();
   if (wave == 0) {
     const int per = (P.E + 63) / 64;
@@ -466,6 +473,9 @@ void moe_gemm_kernel(const GemmParams P) {
       const int r = c / cpr, ch = c % cpr, j0 = ch * 8;
       const int a = s_slot[r];
       u32x4_t v4 = zero_u32x4();
+      // (the LDS copies of rank and scaling would save a vector load here, but on the
+      // 128x256 down tile their live ranges spill into the expand loop: prefill down GEMM
+      // 446 -> 493 us)
       if (a >= 0 && j0 < P.rank[a]) {
         const int ra_rank = P.rank[a];
         const float sc = P.scaling[a];
@@ -624,18 +634,23 @@ void moe_gemm_kernel(const GemmParams P) {
             bl + ((size_t)(P.lora_w_shared ? 0 : e_late) * P.N + wr) * ra_rank + j0);
       }
     };
-    // packed row rr of the slot set bmask -> (slot, rank index); loops over the slot bits
-    // instead of indexing per-batch arrays, which would live in scratch
-    auto locate = [&](int bmask, int rr, int &a, int &j) {
+    // packed row rr of the slot set bmask -> (slot, rank index, slot rank); loops over the
+    // slot bits instead of indexing per-batch arrays, which would live in scratch, and
+    // returns the rank so that no caller indexes P.rank with a per-lane slot (a vector
+    // load from the argument block)
+    auto locate = [&](int bmask, int rr, int &a, int &j, int &rk) {
       a = -1;
       j = 0;
+      rk = 0;
       int off = 0;
       for (int m = bmask; m; m &= m - 1) {
         const int s = __ffs(m) - 1;
-        const int need = (P.rank[s] + 15) / 16 * 16;
+        const int r2 = P.rank[s];
+        const int need = (r2 + 15) / 16 * 16;
         if (a < 0 && rr < off + need) {
           a = s;
           j = rr - off;
+          rk = r2;
         }
         off += need;
       }
@@ -833,13 +848,19 @@ void moe_gemm_kernel(const GemmParams P) {
               *reinterpret_cast<const u32x4_t *>(&Hs[r * HP + c8]);
       }
       // v partials of one batch of slots (set bmask, packed rows in a2src): (row fragment,
-      // packed rank fragment) tasks over the waves
+      // packed rank fragment) tasks over the waves.  Each row's own-slot values go to Vs
+      // (fp32 [BM][64] in the A buffers, free after the K loop; 16-column groups XOR-ed
+      // by row / 4), written out once per tile in 16-byte row chunks: under the weight
+      // stream every vector store instruction waits its turn, and 4-byte fragment stores
+      // took eight times as many.
+      float *Vs = reinterpret_cast<float *>(&As[0][0]);
+      static_assert(BM * MOE_LORA_MAX_RANK * 4 <= (int)sizeof(As), "v tile must fit the A buffers");
       auto contract = [&](int bmask, int rows_used, const uint16_t *a2src, bool swizzled) {
         const int nrf = rows_used / 16;
         for (int f = wave; f < (BM / 16) * nrf; f += NT / 64) {
           const int mf = f / nrf, rf = f % nrf;
-          int a, j16;
-          locate(bmask, rf * 16, a, j16);  // first rank index of this fragment
+          int a, j16, rk;
+          locate(bmask, rf * 16, a, j16, rk);  // first rank index of this fragment
           f32x4_t v4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < HC / 32; ++kk) {
@@ -854,8 +875,8 @@ void moe_gemm_kernel(const GemmParams P) {
           for (int i = 0; i < 4; ++i) {
             const int r = mf * 16 + (lane >> 4) * 4 + i;
             const int j = j16 + (lane & 15);
-            if (r < rows && j < P.rank[a] && s_slot[r] == a)
-              P.down_part[((size_t)col * P.R + row0 + r) * P.rmax + j] = v4[i];
+            if (r < rows && j < rk && s_slot[r] == a)
+              Vs[r * MOE_LORA_MAX_RANK + (j ^ (((r >> 2) & 3) << 4))] = v4[i];
           }
         }
       };
@@ -880,16 +901,40 @@ void moe_gemm_kernel(const GemmParams P) {
           __syncthreads();  // previous batch's reads of A2s done
           for (int q = tid; q < rows_used * (HC / 8); q += NT) {
             const int rr = q / (HC / 8), c8 = (q % (HC / 8)) * 8;
-            int a, j;
-            locate(bmask, rr, a, j);
+            // slot of packed row rr selected over the uniform slot bits (pointer and rank
+            // from scalar loads)
+            const uint16_t *src = nullptr;
+            int rk = 0, j = 0, off = 0;
+            for (int m = bmask; m; m &= m - 1) {
+              const int s2 = __ffs(m) - 1;
+              const int r2 = P.rank[s2];
+              const int need = (r2 + 15) / 16 * 16;
+              if (!src && rr < off + need) {
+                src = P.down_a[s2];
+                rk = r2;
+                j = rr - off;
+              }
+              off += need;
+            }
             u32x4_t v = zero_u32x4();
-            if (j < P.rank[a] && icol0 + c8 < P.I)
-              v = *reinterpret_cast<const u32x4_t *>(P.down_a[a] + ((size_t)e * P.rank[a] + j) * P.I +
-                                                      icol0 + c8);
+            if (src && j < rk && icol0 + c8 < P.I)
+              v = *reinterpret_cast<const u32x4_t *>(src + ((size_t)e * rk + j) * P.I + icol0 + c8);
             *reinterpret_cast<u32x4_t *>(&A2s[rr * HP + c8]) = v;
           }
           __syncthreads();
           contract(bmask, rows_used, A2s, false);
+        }
+      }
+      if (fuse_down) {
+        __syncthreads();
+        // chunks of 4 ranks below the row's own rank (rmax is a multiple of 8)
+        for (int q = tid; q < BM * (P.rmax / 4); q += NT) {
+          const int r = q / (P.rmax / 4), j = (q % (P.rmax / 4)) * 4;
+          const int a = r < rows ? s_slot[r] : -1;
+          const int rk = a >= 0 ? s_rank[a] : 0;
+          if (j < rk)
+            *reinterpret_cast<f32x4_t *>(P.down_part + ((size_t)col * P.R + row0 + r) * P.rmax + j) =
+                *reinterpret_cast<const f32x4_t *>(&Vs[r * MOE_LORA_MAX_RANK + (j ^ (((r >> 2) & 3) << 4))]);
         }
       }
     } else if constexpr (MODE == MODE_DOWN) {
