@@ -12,15 +12,16 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 MOE_DEV float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 round-to-nearest-even (NaN kept quiet).
-MOE_DEV uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16 round-to-nearest-even (a NaN stays a NaN): gfx950's v_cvt_pk_bf16_f32,
+// one instruction for two values where the software rounding took five per value.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+MOE_DEV uint32_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-MOE_DEV uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // SwiGLU of one (gate, up) pair: silu(g) * u with silu(g) = g / (1 + e^-g).  Uses the
 // hardware exp2 and reciprocal (a few ulp in fp32, far below the bf16 rounding that

@@ -473,12 +473,10 @@ void moe_gemm_kernel(const GemmParams P) {
       const int r = c / cpr, ch = c % cpr, j0 = ch * 8;
       const int a = s_slot[r];
       u32x4_t v4 = zero_u32x4();
-      // (the LDS copies of rank and scaling would save a vector load here, but on the
-      // 128x256 down tile their live ranges spill into the expand loop: prefill down GEMM
-      // 446 -> 493 us)
-      if (a >= 0 && j0 < P.rank[a]) {
-        const int ra_rank = P.rank[a];
-        const float sc = P.scaling[a];
+      // The chunk test reads the rank from the LDS table, so that the partial loads do not
+      // wait for a load of it: the rank and scaling loads below (vector loads, a is per
+      // lane) travel with them, one round trip instead of two.
+      if (a >= 0 && j0 < s_rank[a]) {
         const f32x4_t *src = reinterpret_cast<const f32x4_t *>(P.part + (size_t)(row0 + r) * P.rmax + j0);
         const size_t split_stride = (size_t)P.R * P.rmax / 4;  // in f32x4 units
         float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -500,6 +498,8 @@ void moe_gemm_kernel(const GemmParams P) {
               v[4 + t] += x[q][1][t];
             }
         }
+        const int ra_rank = P.rank[a];
+        const float sc = P.scaling[a];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float lo = (j0 + 2 * q < ra_rank) ? v[2 * q] * sc : 0.f;
