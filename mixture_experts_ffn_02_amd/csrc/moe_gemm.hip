@@ -938,12 +938,17 @@ void moe_gemm_kernel(const GemmParams P) {
         }
       }
     } else if constexpr (MODE == MODE_DOWN) {
-      // bf16 output tile through LDS (pitch OP) for 16-byte row-chunk stores; a tile whose
-      // rows do not fit the B buffers at once goes in two row halves
-      constexpr int OP = BN + 8;
+      // bf16 output tile through LDS for 16-byte row-chunk stores.  Rows are BN elements
+      // apart with the 16-column groups XOR-ed by (row / 4) % 4, so that the four row
+      // groups of a fragment store land in different banks without padding, and the whole
+      // tile fits the B buffers at once (the padded 128x256 tile went in two halves, one
+      // barrier pair each)
+      constexpr int OP = BN;
       constexpr int RH = (BM * OP <= 2 * BN * BK) ? BM : BM / 2;
       static_assert(RH * OP <= 2 * BN * BK && RH % WTM == 0, "output rows must fit the B buffers");
+      static_assert(BN % 64 == 0, "the column swizzle permutes 16-column groups within 64");
       uint16_t *Os = reinterpret_cast<uint16_t *>(Bs);
+      auto os_col = [](int r, int c) { return c ^ (((r >> 2) & 3) << 4); };
 #pragma unroll
       for (int h = 0; h < BM / RH; ++h) {
         if (h) __syncthreads();  // the previous half has been read
@@ -956,7 +961,7 @@ void moe_gemm_kernel(const GemmParams P) {
               for (int i = 0; i < 4; ++i) {
                 const int r = wm * WTM - h * RH + fm * 16 + (lane >> 4) * 4 + i;
                 const int c = wn * WTN + fn * 16 + (lane & 15);
-                Os[r * OP + c] = (uint16_t)f32_to_bf16(acc[fm][fn][i]);
+                Os[r * OP + os_col(r, c)] = (uint16_t)f32_to_bf16(acc[fm][fn][i]);
               }
         }
         __syncthreads();
@@ -965,7 +970,7 @@ void moe_gemm_kernel(const GemmParams P) {
           const int n = col * BN + c8;  // N is a multiple of 8: a chunk is all in or all out
           if (h * RH + r < rows && n < P.N)
             *reinterpret_cast<u32x4_t *>(P.out_bf16 + (size_t)(row0 + h * RH + r) * P.N + n) =
-                *reinterpret_cast<const u32x4_t *>(&Os[r * OP + c8]);
+                *reinterpret_cast<const u32x4_t *>(&Os[r * OP + os_col(r, c8)]);
         }
       }
     } else {
