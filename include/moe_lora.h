@@ -69,7 +69,7 @@ typedef enum {
 typedef struct {
   int32_t num_tokens;  /* T >= 0 */
   int32_t hidden;      /* H, multiple of 8 */
-  int32_t inter;       /* I, multiple of 8 (expert intermediate size) */
+  int32_t inter;       /* I, multiple of 8 (expert intermediate size); 2*I*H < 2^30 */
   int32_t num_experts; /* E in [1, MOE_LORA_MAX_EXPERTS] */
   int32_t top_k;       /* k in [1, min(E, MOE_LORA_MAX_TOPK)] */
 } moe_lora_dims;

@@ -18,6 +18,8 @@ int check_dims(const moe_lora_dims *d) {
     return MOE_LORA_ERR_INVALID_ARGUMENT;
   if ((d->hidden % 8) != 0 || (d->inter % 8) != 0) return MOE_LORA_ERR_UNSUPPORTED;
   if ((long long)d->num_tokens * d->top_k > (1ll << 30)) return MOE_LORA_ERR_UNSUPPORTED;
+  // one expert's gate_up matrix stays below 2 GiB (the GEMMs address it with 32-bit offsets)
+  if ((long long)2 * d->inter * d->hidden >= (1ll << 30)) return MOE_LORA_ERR_UNSUPPORTED;
   return MOE_LORA_OK;
 }
 

@@ -326,19 +326,26 @@ void moe_gemm_kernel(const GemmParams P) {
                        u32x4_t(&xb)[B_IT], auto nt, auto pk) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) xa[i] = *reinterpret_cast<const u32x4_t *>(a_ptr[i] + k0);
+    // B through a raw buffer resource on the expert's matrix: a 32-bit per-lane byte
+    // offset that does not change along K plus the K step's byte offset in a scalar
+    // register.  Plain global loads kept one 64-bit address per lane for every chunk of
+    // every register stage (a quarter of the register file on the 16-row tiles).  One
+    // expert matrix is < 2 GiB (checked by the host), so both offsets fit 32 bits.
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(bbase), (short)0, 0x7fffffff, 0x00020000);
+    const int soff = decltype(pk)::value ? (k0 / BK) * P.N * BK * 2 : k0 * 2;
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
-      const u32x4_t *src;
+      uint32_t lo;
       if constexpr (decltype(pk)::value) {
-        src = reinterpret_cast<const u32x4_t *>(bbase + b_pk[i] + (size_t)(k0 / BK) * P.N * BK);
+        lo = (uint32_t)b_pk[i] * 2u;
       } else {
         const int wr = (b_wrow[i] >= 0 && b_wrow[i] < bcount) ? b_wrow[i] : 0;
-        src = reinterpret_cast<const u32x4_t *>(bbase + (size_t)wr * P.K + k0 + b_c8[i] * 8);
+        lo = ((uint32_t)wr * (uint32_t)P.K + (uint32_t)b_c8[i] * 8u) * 2u;
       }
-      if constexpr (decltype(nt)::value)
-        xb[i] = __builtin_nontemporal_load(src);
-      else
-        xb[i] = *src;
+      // aux 2: non-temporal (the weights are streamed once)
+      xb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rsrc, lo, soff, decltype(nt)::value ? 2 : 0));
     }
   };
   // ragged K tail and padding rows zeroed (used once, off the steady state)
@@ -634,17 +641,19 @@ void moe_gemm_kernel(const GemmParams P) {
             bl + ((size_t)(P.lora_w_shared ? 0 : e_late) * P.N + wr) * ra_rank + j0);
       }
     };
-    // packed row rr of the slot set bmask -> (slot, rank index, slot rank); loops over the
-    // slot bits instead of indexing per-batch arrays, which would live in scratch, and
-    // returns the rank so that no caller indexes P.rank with a per-lane slot (a vector
-    // load from the argument block)
+    // packed row rr of the slot set bmask -> (slot, rank index, slot rank); walks the slots
+    // with constant indices (the ranks stay in scalar registers, where a walk over the set
+    // bits reloaded them from the argument block on every call: multi-adapter gate_up
+    // 173 -> 170 us) and returns the rank, so that no caller indexes P.rank with a
+    // per-lane slot (a vector load from the argument block)
     auto locate = [&](int bmask, int rr, int &a, int &j, int &rk) {
       a = -1;
       j = 0;
       rk = 0;
       int off = 0;
-      for (int m = bmask; m; m &= m - 1) {
-        const int s = __ffs(m) - 1;
+#pragma unroll
+      for (int s = 0; s < MOE_LORA_MAX_SLOTS; ++s) {
+        if (!((bmask >> s) & 1)) continue;
         const int r2 = P.rank[s];
         const int need = (r2 + 15) / 16 * 16;
         if (a < 0 && rr < off + need) {

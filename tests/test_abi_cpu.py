@@ -83,6 +83,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (valida
     ((-1, 256, 128, 8, 2), _lib.ERR_INVALID_ARGUMENT),    # negative T
     ((16, 252, 128, 8, 2), _lib.ERR_UNSUPPORTED),         # H not a multiple of 8
     ((16, 256, 100, 8, 2), _lib.ERR_UNSUPPORTED),         # I not a multiple of 8
+    ((16, 32768, 16384, 8, 2), _lib.ERR_UNSUPPORTED),     # 2*I*H = 2^30: 32-bit offsets
 ])
 def test_bad_dims_rejected_before_launch(dims, status):
     lib = pkg.load()
