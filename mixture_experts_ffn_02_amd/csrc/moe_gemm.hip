@@ -469,7 +469,9 @@ void moe_gemm_kernel(const GemmParams P) {
   // the partials of up to G splits loaded together (one memory latency per group) and
   // summed in split order.
   auto build_xs = [&]() {
-    constexpr int G = PF >= 4 ? 4 : 8;  // four register stages in flight leave room for 4
+    // splits loaded per round trip (decode: the gate_up shrink has 7 splits, the down
+    // expand 12; 4 at a time on 16-row tiles cost 1 % at decode against 8)
+    constexpr int G = 8;
     const int cpr = P.rmax >> 3;  // 8-rank chunks that can hold data (rmax is a multiple of 8)
     // chunks past rmax are zero
     for (int c = tid; c < BM * (8 - cpr); c += NT) {
