@@ -84,6 +84,9 @@ struct GemmParams {
   int w_packed;       // w is in the tile-packed layout (128-row x 64-column blocks)
   const float *part;                            // ext A source [splits][R][rmax]
   int part_splits;
+  // ext A source already reduced over the splits, scaled and rounded: bf16 [R][rmax]
+  // (zero past each row's rank); when set, part / part_splits are not read
+  const uint16_t *part_bf16;
   int rmax;
   uint16_t *out_bf16;
   float *out_f32;
@@ -477,6 +480,17 @@ void moe_gemm_kernel(const GemmParams P) {
     for (int c = tid; c < BM * (8 - cpr); c += NT) {
       const int r = c / (8 - cpr), ch = cpr + c % (8 - cpr);
       *reinterpret_cast<u32x4_t *>(&Xs[lds_off(r, ch)]) = zero_u32x4();
+    }
+    if (P.part_bf16) {
+      for (int c = tid; c < BM * cpr; c += NT) {
+        const int r = c / cpr, ch = c % cpr, j0 = ch * 8;
+        const int a = s_slot[r];
+        u32x4_t v4 = zero_u32x4();
+        if (a >= 0 && j0 < s_rank[a])
+          v4 = *reinterpret_cast<const u32x4_t *>(P.part_bf16 + (size_t)(row0 + r) * P.rmax + j0);
+        *reinterpret_cast<u32x4_t *>(&Xs[lds_off(r, ch)]) = v4;
+      }
+      return;
     }
     for (int c = tid; c < BM * cpr; c += NT) {
       const int r = c / cpr, ch = c % cpr, j0 = ch * 8;
@@ -1125,6 +1139,55 @@ int launch_shrink(const GemmParams &P0, int bm, int splits, hipStream_t s) {
 // gate_up LoRA delta D joined right before SwiGLU (bf16 PR, Files-changed table,
 // activation row: the delta is added before SwiGLU; the activation output feeds the
 // down LoRA).  G and D are fp32 [R, 2I] with rows [gate | up]; one thread per 4 columns.
+// Split partials of the fused down shrink reduced once per step for the down GEMM's
+// expand: out[p][j] = bf16(s_a * sum over splits of part[split][p][j]) for j below the
+// rank of row p's slot, zero elsewhere; the splits are summed in ascending order, as the
+// down GEMM sums them itself when it reads the partials directly (so both give the same
+// bits).  One thread per (row, 8-rank chunk).
+struct SlotRanks {
+  int rank[MOE_LORA_MAX_SLOTS];
+  float scaling[MOE_LORA_MAX_SLOTS];
+};
+
+__global__ __launch_bounds__(256) void reduce_part_kernel(const float *__restrict__ part, int splits, int R,
+                                                          int rmax, const int32_t *__restrict__ row_slot,
+                                                          const SlotRanks sr, uint16_t *__restrict__ out) {
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = rmax / 8;
+  if (q >= (long long)R * cpr) return;
+  const int p = (int)(q / cpr), j0 = (int)(q % cpr) * 8;
+  const int a = row_slot[p];
+  int rk = 0;
+  float sc = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < MOE_LORA_MAX_SLOTS; ++s2)
+    if (a == s2) {
+      rk = sr.rank[s2];
+      sc = sr.scaling[s2];
+    }
+  u32x4_t v4 = zero_u32x4();
+  if (j0 < rk) {
+    const f32x4_t *src = reinterpret_cast<const f32x4_t *>(part + (size_t)p * rmax + j0);
+    const size_t stride = (size_t)R * rmax / 4;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < splits; ++sp) {
+      const f32x4_t x0 = src[(size_t)sp * stride], x1 = src[(size_t)sp * stride + 1];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[t] += x0[t];
+        v[4 + t] += x1[t];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float lo = (j0 + 2 * c < rk) ? v[2 * c] * sc : 0.f;
+      const float hi = (j0 + 2 * c + 1 < rk) ? v[2 * c + 1] * sc : 0.f;
+      v4[c] = pack_bf16x2(lo, hi);
+    }
+  }
+  *reinterpret_cast<u32x4_t *>(out + (size_t)p * rmax + j0) = v4;
+}
+
 __global__ __launch_bounds__(256) void swiglu_join_kernel(const float *__restrict__ G,
                                                           const float *__restrict__ D,
                                                           uint16_t *__restrict__ act, int R, int I) {
@@ -1172,10 +1235,18 @@ int get_events(StreamEvents *&out) {
 constexpr int kTwoStreamMaxT = 256;  // decomposed-path buffers exist up to this many tokens
 
 struct FwdLayout {
-  size_t u_part = 0, act = 0, v_part = 0, g = 0, dlt = 0, row_slot = 0, total = 0;
+  size_t u_part = 0, act = 0, v_part = 0, v_red = 0, g = 0, dlt = 0, row_slot = 0, total = 0;
   int splits1 = 0, steps1 = 0, splits2 = 0, shrink2_splits = 0, steps2 = 0, rmax = 0;
   bool decomposed = false;
 };
+
+// A down expand whose partials come in more splits than one round trip of build_xs loads,
+// and whose n-tiles would re-read at least kReduceMinBytes of them in all, is fed by one
+// reduction per step instead (multi-adapter T=256: 100 MB of re-reads, step -1.6 %;
+// DeepSeek-V3-sized: 1.9 GB, -1.9 %).  Below that the extra launch costs more than it
+// saves (decode T=64: 6 MB, +1.3 %).
+constexpr int kReduceMinSplits = 8;
+constexpr long long kReduceMinBytes = 32ll << 20;
 
 FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
   FwdLayout L;
@@ -1198,6 +1269,8 @@ FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
     off = align256(off + (size_t)L.splits2 * R * L.rmax * sizeof(float));
     L.row_slot = off;
     off = align256(off + R * sizeof(int32_t));
+    L.v_red = off;
+    off = align256(off + R * L.rmax * sizeof(uint16_t));
   }
   if (has_lora && d.num_tokens <= kTwoStreamMaxT && (d.inter % 4) == 0) {
     L.decomposed = true;
@@ -1368,6 +1441,22 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       P.part = v_part;
       P.part_splits = decomposed ? L.shrink2_splits : gateup_ncols(bm, d.inter);
       P.row_slot = row_slot;
+      const long long down_ntiles = cdiv(d.hidden, bm >= 128 ? 256 : 128);
+      const long long reread = down_ntiles * P.part_splits * R * L.rmax * (long long)sizeof(float);
+      if (P.part_splits > kReduceMinSplits && reread >= kReduceMinBytes) {
+        // every down n-tile would re-read all splits: reduce them once
+        uint16_t *v_red = reinterpret_cast<uint16_t *>(wsb + L.v_red);
+        SlotRanks sr{};
+        for (int s = 0; s < lora->num_slots; ++s) {
+          sr.rank[s] = lora->rank[s];
+          sr.scaling[s] = lora->scaling[s];
+        }
+        const long long nthr = (long long)R * (L.rmax / 8);
+        reduce_part_kernel<<<dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, main>>>(
+            v_part, P.part_splits, R, L.rmax, row_slot, sr, v_red);
+        if (hipGetLastError() != hipSuccess) return ST_HIP;
+        P.part_bf16 = v_red;
+      }
     }
     P.out_bf16 = y_perm;
     if ((st = launch_gemm<MODE_DOWN>(P, bm, main)) != ST_OK) return st;
