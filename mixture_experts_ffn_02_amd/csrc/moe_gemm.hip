@@ -1240,12 +1240,12 @@ struct FwdLayout {
   bool decomposed = false;
 };
 
-// A down expand whose partials come in more splits than one round trip of build_xs loads,
-// and whose n-tiles would re-read at least kReduceMinBytes of them in all, is fed by one
-// reduction per step instead (multi-adapter T=256: 100 MB of re-reads, step -1.6 %;
-// DeepSeek-V3-sized: 1.9 GB, -1.9 %).  Below that the extra launch costs more than it
-// saves (decode T=64: 6 MB, +1.3 %).
-constexpr int kReduceMinSplits = 8;
+// A down expand whose partials come in more than four splits, and whose n-tiles would
+// re-read at least kReduceMinBytes of them in all, is fed by one reduction per step
+// instead (prefill T=8192: 6 splits, 192 MB of re-reads, step -1.1 %; multi-adapter
+// T=256: 12 and 100 MB, -1.1 %; DeepSeek-V3-sized: 32 and 1.9 GB, -1.9 %).  Below that
+// the extra launch costs more than it saves (decode T=64: 6 MB, +1.3 %).
+constexpr int kReduceMinSplits = 4;
 constexpr long long kReduceMinBytes = 32ll << 20;
 
 FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
