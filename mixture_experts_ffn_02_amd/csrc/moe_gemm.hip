@@ -875,9 +875,9 @@ void moe_gemm_kernel(const GemmParams P) {
       // v partials of one batch of slots (set bmask, packed rows in a2src): (row fragment,
       // packed rank fragment) tasks over the waves.  Each row's own-slot values go to Vs
       // (fp32 [BM][64] in the A buffers, free after the K loop; 16-column groups XOR-ed
-      // by row / 4), written out once per tile in 16-byte row chunks: under the weight
-      // stream every vector store instruction waits its turn, and 4-byte fragment stores
-      // took eight times as many.
+      // by row / 4), written out once per tile in 16-byte row chunks of the row's own
+      // rank (an eighth of the store instructions of 4-byte fragment stores; the time
+      // the contraction took was its argument-block loads, see locate()).
       float *Vs = reinterpret_cast<float *>(&As[0][0]);
       static_assert(BM * MOE_LORA_MAX_RANK * 4 <= (int)sizeof(As), "v tile must fit the A buffers");
       auto contract = [&](int bmask, int rows_used, const uint16_t *a2src, bool swizzled) {
