@@ -9,9 +9,11 @@ this package imports nothing from the product path.
 from .moe_lora_ref import (  # noqa: F401
     Adapter,
     bf16_bits_to_f64,
+    e4m3_to_f64,
     expert_sort,
     finalize,
     forward_permuted,
+    fp8_block_weights,
     layer,
     layer_sampled,
     permute_rows,

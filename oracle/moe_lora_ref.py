@@ -45,6 +45,12 @@ Readings of points the pages leave open (each is also listed in the design notes
   * shared-outer LoRA ([P1] section 2): the gate_up A and the down B are shared by all
     experts, the gate_up B and the down A are per expert; rounding and weighting as in
     the routed layer (the down delta is added to the expert output before finalize).
+  * FP8 expert weights ([P2] title and Optimizations: the LoRA deltas are applied around
+    an FP8 fused MoE; the pages fix no format): OCP E4M3 codes (sign, 4 exponent bits
+    with bias 7, 3 mantissa bits, subnormals, 0x7f / 0xff NaN, no infinities), one fp32
+    scale per 128 x 128 block of each expert matrix, weight = value(code) * scale of its
+    block.  The layer is then the bf16 layer's definition on those weights; the LoRA
+    matrices stay bf16.
 """
 
 from __future__ import annotations
@@ -61,6 +67,33 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact bf16 -> fp64: a bf16 pattern is the upper half of an fp32 pattern."""
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Value of each OCP E4M3 code (uint8) in fp64, written out from the format's fields."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    exp = (c >> 3) & 0xF
+    man = (c & 0x7).astype(np.float64)
+    normal = sign * np.ldexp(1.0 + man / 8.0, exp - 7)
+    subnormal = sign * np.ldexp(man / 8.0, -6)
+    v = np.where(exp == 0, subnormal, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def fp8_block_weights(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
+    """One expert matrix [N, K] from E4M3 codes [N, K] and fp32 block scales
+    [ceil(N / block), ceil(K / block)]: w[n, k] = value(codes[n, k]) * scales[n // block, k // block]."""
+    v = e4m3_to_f64(codes)
+    N, K = v.shape
+    s = np.asarray(scales, dtype=np.float64)
+    return v * s[np.arange(N)[:, None] // block, np.arange(K)[None, :] // block]
+
+
+def _weights_f64(w: np.ndarray) -> np.ndarray:
+    """Expert matrix as fp64: bf16 bit patterns (uint16/int16) are decoded; fp64 arrays (an
+    FP8 matrix already dequantized by fp8_block_weights) are used as they are."""
+    return w if np.asarray(w).dtype == np.float64 else bf16_bits_to_f64(w)
 
 
 def silu(g: np.ndarray) -> np.ndarray:
@@ -206,8 +239,8 @@ def _expert_rows(X: np.ndarray, e: int, I: int, w_gate_up: BitsFn, w_down: BitsF
         h = silu(g[:I]) * g[I:]
         y = W2[e] h + s_a B2[a][e] (A2[a][e] h)      (down LoRA on the activation)
     """
-    W1 = bf16_bits_to_f64(w_gate_up(e))
-    W2 = bf16_bits_to_f64(w_down(e))
+    W1 = _weights_f64(w_gate_up(e))
+    W2 = _weights_f64(w_down(e))
     G = X @ W1.T
     for a, ad in enumerate(adapters):
         rows = np.nonzero(row_slot == a)[0]

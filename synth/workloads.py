@@ -46,6 +46,10 @@ _T_A2 = 22
 _T_B2 = 23
 _T_A1_SHARED = 24
 _T_B2_SHARED = 25
+_T_W1_FP8 = 30
+_T_W2_FP8 = 31
+_T_W1_SCALE = 32
+_T_W2_SCALE = 33
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -244,6 +248,39 @@ class Workload:
         return self._normal_bf16((c.H, c.slots[a].rank), c.lora_b_std, _T_B2_SHARED, a)
 
     # -- stacked forms ---------------------------------------------------
+    # -- FP8 expert weights (E4M3 codes + one fp32 scale per 128 x 128 block) --------
+    def _fp8_codes(self, shape, tensor: int, e: int) -> np.ndarray:
+        """Random E4M3 codes: uniform sign and mantissa, exponent field 4..7 (magnitudes
+        0.125 .. 1.875 before scaling); no NaN codes."""
+        g = self._rng(tensor, 0, e)
+        sign = g.integers(0, 2, size=shape, dtype=np.uint8) << 7
+        exp = g.integers(4, 8, size=shape, dtype=np.uint8) << 3
+        man = g.integers(0, 8, size=shape, dtype=np.uint8)
+        return sign | exp | man
+
+    def _fp8_scales(self, n: int, k: int, tensor: int, e: int, pow2: bool) -> np.ndarray:
+        """fp32 block scales around w_std: uniform in [0.5, 1.5) * w_std, or (pow2) the
+        power of two nearest w_std times 2^{-1, 0, 1}."""
+        c = self.cfg
+        shape = ((n + 127) // 128, (k + 127) // 128)
+        g = self._rng(tensor, 0, e)
+        if pow2:
+            base = np.round(np.log2(c.w_std))
+            return np.ldexp(np.ones(shape, np.float32), (base + g.integers(-1, 2, size=shape)).astype(np.int32))
+        return (g.uniform(0.5, 1.5, size=shape) * c.w_std).astype(np.float32)
+
+    def w_gate_up_fp8(self, e: int, pow2: bool = False) -> tuple:
+        """Expert e's gate_up weight as (codes uint8 [2I, H], scales fp32 [2I/128, H/128])."""
+        c = self.cfg
+        return (self._fp8_codes((2 * c.I, c.H), _T_W1_FP8, e),
+                self._fp8_scales(2 * c.I, c.H, _T_W1_SCALE, e, pow2))
+
+    def w_down_fp8(self, e: int, pow2: bool = False) -> tuple:
+        """Expert e's down weight as (codes uint8 [H, I], scales fp32 [H/128, I/128])."""
+        c = self.cfg
+        return (self._fp8_codes((c.H, c.I), _T_W2_FP8, e),
+                self._fp8_scales(c.H, c.I, _T_W2_SCALE, e, pow2))
+
     def _stack(self, fn, count: int, shape, experts: Optional[Sequence[int]] = None) -> np.ndarray:
         experts = list(range(count)) if experts is None else list(experts)
         out = np.empty((len(experts),) + tuple(shape), dtype=np.uint16)
