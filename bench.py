@@ -20,6 +20,7 @@ import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -256,6 +257,31 @@ def main():
         t_graph = (time.perf_counter() - t0) / args.steps
         del graph
 
+    t_fp8, fp8_gate_up_ms = None, None
+    fp8_ok = cfg.H % 128 == 0 and cfg.I % 128 == 0 and cfg.E * 3 * cfg.I * cfg.H <= (1 << 31)
+    if fp8_ok:
+        log("timing LoRA on with FP8 expert weights (E4M3 codes, fp32 scale per 128x128 block)")
+
+        def fp8_stack(fn):
+            pairs = [None] * cfg.E
+
+            def fill(e):
+                pairs[e] = fn(e)
+
+            with ThreadPoolExecutor(8) as ex:
+                list(ex.map(fill, range(cfg.E)))
+            codes = torch.from_numpy(np.stack([p[0] for p in pairs])).to(dev)
+            scales = torch.from_numpy(np.stack([p[1] for p in pairs])).to(dev)
+            return codes, scales
+
+        c1, s1 = fp8_stack(wl.w_gate_up_fp8)
+        c2, s2 = fp8_stack(wl.w_down_fp8)
+        layer_fp8 = ml.MoELoRALayer(cfg.H, cfg.I, cfg.E, cfg.top_k, c1, c2, routing, cfg.n_group,
+                                    cfg.topk_group, cfg.routed_scaling_factor, bias, gather_on_load=True,
+                                    w_gate_up_scale=s1, w_down_scale=s2)
+        t_fp8, fp8_gate_up_ms = timed(layer_fp8, lora, args.steps, args.warmup, gate_up_events=True)
+        del layer_fp8, c1, c2, s1, s2
+
     # realized routing -> algorithmic bytes and flops
     layer(x, logits, lora)
     torch.cuda.synchronize()
@@ -280,6 +306,9 @@ def main():
     layer_bytes = w_bytes_gu + w_bytes_dn + lora_all + io_bytes
     layer_flops = 2 * R * 3 * I * H + lora_flops
     gate_up_bytes = w_bytes_gu + lora_gu + T * H * 2 + R * I * 2
+    # FP8 weights: one byte per weight plus one fp32 scale per 128 x 128 block
+    gate_up_bytes_fp8 = (active * 2 * I * H + active * (2 * I // 128) * (H // 128) * 4 + lora_gu
+                         + T * H * 2 + R * I * 2)
     gate_up_flops = 2 * R * 2 * I * H + (lora_flops * 2 * H // (2 * H + 3 * I) if lora_flops else 0)
 
     tok_on = T / t_on
@@ -325,6 +354,13 @@ def main():
         "ms_per_step_two_stream": round(t_two * 1e3, 4) if t_two else None,
         "ms_per_step_graph_replay": round(t_graph * 1e3, 4) if t_graph else None,
         "ms_per_step_row_major_weights": round(t_rm * 1e3, 4) if t_rm else None,
+        "fp8_weights": None if t_fp8 is None else {
+            "ms_per_step": round(t_fp8 * 1e3, 4), "value": round(T / t_fp8, 1), "unit": "tokens/s",
+            "weights": "E4M3 codes, fp32 scale per 128x128 block; LoRA bf16",
+            "gate_up_us": round(fp8_gate_up_ms * 1e3, 2),
+            "gate_up_algorithmic_bytes": int(gate_up_bytes_fp8),
+            "gate_up_achieved_gbs": round(gate_up_bytes_fp8 / (fp8_gate_up_ms * 1e-3) / 1e9, 1),
+            "gate_up_hbm_frac": round(gate_up_bytes_fp8 / (fp8_gate_up_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "shared_outer": ({"ms_per_step": round(t_shared * 1e3, 4), "value": round(T / t_shared, 1),
                           "lora_ratio": round(t_off / t_shared, 4)} if t_shared else None),
         "layer_roofline": {

@@ -198,6 +198,27 @@ int moe_lora_forward(const moe_lora_dims *dims, const uint16_t *x, const uint16_
                      moe_lora_stream_t main, moe_lora_stream_t side,
                      const moe_lora_options *opts);
 
+/* ---------------------------------------------------------------- forward, FP8 weights
+ * moe_lora_forward with FP8 expert weights (fast-path PR, title and Optimizations: the
+ * LoRA deltas are applied around an FP8 fused MoE; the LoRA matrices stay bf16).
+ *   w_gate_up [E, 2I, H], w_down [E, H, I]: OCP E4M3 codes, one byte per weight
+ *     (sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7f / 0xff are NaN).
+ *   w_gate_up_scale [E, 2I/128, H/128], w_down_scale [E, H/128, I/128]: fp32, one scale
+ *     per 128 x 128 block; weight = value(code) * scale of its block.
+ * Each weight is rounded to bf16 once (fp32 product, round to nearest even) before the
+ * bf16 MFMA; everything else is as in moe_lora_forward, whose workspace size applies.
+ * All four weight pointers are device pointers, 16-byte aligned (else
+ * MOE_LORA_ERR_INVALID_ARGUMENT).  Requires hidden % 128 == 0 and inter % 128 == 0, and
+ * runs the fused path only: opts->packed_weights != 0 or opts->force_path == 2 ->
+ * MOE_LORA_ERR_UNSUPPORTED; a side stream is not used. */
+int moe_lora_forward_fp8(const moe_lora_dims *dims, const uint16_t *x, const uint16_t *x_perm,
+                         const int32_t *expert_offsets, const int32_t *permuted_to_expanded,
+                         const uint8_t *w_gate_up, const float *w_gate_up_scale,
+                         const uint8_t *w_down, const float *w_down_scale,
+                         const moe_lora_adapters *lora, uint16_t *y_perm, void *ws, size_t ws_bytes,
+                         moe_lora_stream_t main, moe_lora_stream_t side,
+                         const moe_lora_options *opts);
+
 /* ---------------------------------------------------------------- pack weights
  * Tile-packed copies of the expert weights for moe_lora_forward with
  * opts->packed_weights = 1.  The grouped GEMMs read each expert's weights one 64-wide K

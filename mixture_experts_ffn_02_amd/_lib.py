@@ -36,6 +36,7 @@ EXPORTED = (
     "moe_lora_permute",
     "moe_lora_forward_workspace_size",
     "moe_lora_forward",
+    "moe_lora_forward_fp8",
     "moe_lora_pack_weights",
     "moe_lora_finalize",
 )
@@ -105,6 +106,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_lora_forward.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, POINTER(Adapters), c_void_p, c_void_p,
                                      c_size_t, c_void_p, c_void_p, POINTER(Options)]
+    lib.moe_lora_forward_fp8.restype = c_int
+    lib.moe_lora_forward_fp8.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, POINTER(Adapters),
+                                         c_void_p, c_void_p, c_size_t, c_void_p, c_void_p,
+                                         POINTER(Options)]
     lib.moe_lora_pack_weights.restype = c_int
     lib.moe_lora_pack_weights.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
                                           c_void_p]

@@ -156,11 +156,16 @@ size_t moe_lora_forward_workspace_size(const moe_lora_dims *d, const moe_lora_ad
   return moe::forward_workspace_size(*d, lora);
 }
 
-int moe_lora_forward(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x_perm,
-                     const int32_t *expert_offsets, const int32_t *p2e, const uint16_t *w_gate_up,
-                     const uint16_t *w_down, const moe_lora_adapters *lora, uint16_t *y_perm,
-                     void *ws, size_t ws_bytes, moe_lora_stream_t main, moe_lora_stream_t side,
-                     const moe_lora_options *opts) {
+namespace {
+
+// argument checks and launch shared by the bf16 and FP8 forward entry points (the FP8 one
+// passes the block scales; weights are then byte arrays of E4M3 codes)
+int forward_checked(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x_perm,
+                    const int32_t *expert_offsets, const int32_t *p2e, const void *w_gate_up,
+                    const void *w_down, const float *w1_scale, const float *w2_scale,
+                    const moe_lora_adapters *lora, uint16_t *y_perm, void *ws, size_t ws_bytes,
+                    moe_lora_stream_t main, moe_lora_stream_t side, const moe_lora_options *opts,
+                    bool fp8) {
   int st = check_dims(d);
   if (st != MOE_LORA_OK) return st;
   if ((st = check_lora(lora)) != MOE_LORA_OK) return st;
@@ -168,6 +173,10 @@ int moe_lora_forward(const moe_lora_dims *d, const uint16_t *x, const uint16_t *
   if (opts && (opts->packed_weights < 0 || opts->packed_weights > 3)) return MOE_LORA_ERR_INVALID_ARGUMENT;
   if (opts && opts->packed_weights && (d->hidden % 128 != 0 || d->inter % 64 != 0))
     return MOE_LORA_ERR_UNSUPPORTED;
+  if (fp8) {
+    if (d->hidden % 128 != 0 || d->inter % 128 != 0) return MOE_LORA_ERR_UNSUPPORTED;
+    if (opts && (opts->packed_weights || opts->force_path == 2)) return MOE_LORA_ERR_UNSUPPORTED;
+  }
   if (d->num_tokens == 0) return MOE_LORA_OK;
   if (!x && !x_perm) return MOE_LORA_ERR_INVALID_ARGUMENT;
   if ((x && !aligned16(x)) || (x_perm && !aligned16(x_perm))) return MOE_LORA_ERR_INVALID_ARGUMENT;
@@ -176,12 +185,35 @@ int moe_lora_forward(const moe_lora_dims *d, const uint16_t *x, const uint16_t *
   if (!aligned16(expert_offsets) || !aligned16(p2e) || !aligned16(w_gate_up) ||
       !aligned16(w_down) || !aligned16(y_perm))
     return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (fp8 && (!w1_scale || !w2_scale || !aligned16(w1_scale) || !aligned16(w2_scale)))
+    return MOE_LORA_ERR_INVALID_ARGUMENT;
   const size_t need = moe::forward_workspace_size(*d, lora);
   if (ws_bytes < need) return MOE_LORA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && (!ws || !aligned16(ws))) return MOE_LORA_ERR_INVALID_ARGUMENT;
-  return moe::launch_forward(*d, x, x_perm, expert_offsets, p2e, w_gate_up, w_down, lora, y_perm,
-                             ws, ws_bytes, reinterpret_cast<hipStream_t>(main),
-                             reinterpret_cast<hipStream_t>(side), opts);
+  return moe::launch_forward(*d, x, x_perm, expert_offsets, p2e, static_cast<const uint16_t *>(w_gate_up),
+                             static_cast<const uint16_t *>(w_down), lora, y_perm, ws, ws_bytes,
+                             reinterpret_cast<hipStream_t>(main), reinterpret_cast<hipStream_t>(side), opts,
+                             fp8 ? w1_scale : nullptr, fp8 ? w2_scale : nullptr);
+}
+
+}  // namespace
+
+int moe_lora_forward(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x_perm,
+                     const int32_t *expert_offsets, const int32_t *p2e, const uint16_t *w_gate_up,
+                     const uint16_t *w_down, const moe_lora_adapters *lora, uint16_t *y_perm,
+                     void *ws, size_t ws_bytes, moe_lora_stream_t main, moe_lora_stream_t side,
+                     const moe_lora_options *opts) {
+  return forward_checked(d, x, x_perm, expert_offsets, p2e, w_gate_up, w_down, nullptr, nullptr, lora,
+                         y_perm, ws, ws_bytes, main, side, opts, false);
+}
+
+int moe_lora_forward_fp8(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x_perm,
+                         const int32_t *expert_offsets, const int32_t *p2e, const uint8_t *w_gate_up,
+                         const float *w_gate_up_scale, const uint8_t *w_down, const float *w_down_scale,
+                         const moe_lora_adapters *lora, uint16_t *y_perm, void *ws, size_t ws_bytes,
+                         moe_lora_stream_t main, moe_lora_stream_t side, const moe_lora_options *opts) {
+  return forward_checked(d, x, x_perm, expert_offsets, p2e, w_gate_up, w_down, w_gate_up_scale,
+                         w_down_scale, lora, y_perm, ws, ws_bytes, main, side, opts, true);
 }
 
 int moe_lora_finalize(const moe_lora_dims *d, const uint16_t *y_perm, const float *topk_weights,

@@ -16,6 +16,7 @@ MOE_DEV float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 // one instruction for two values where the software rounding took five per value.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 MOE_DEV uint32_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {

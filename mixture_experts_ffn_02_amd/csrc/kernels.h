@@ -45,6 +45,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
                    const int32_t *offsets, const int32_t *p2e, const uint16_t *w1,
                    const uint16_t *w2, const moe_lora_adapters *lora, uint16_t *y_perm, void *ws,
                    size_t ws_bytes, hipStream_t main, hipStream_t side,
-                   const moe_lora_options *opts);
+                   const moe_lora_options *opts, const float *w1_scale = nullptr,
+                   const float *w2_scale = nullptr);
 
 }  // namespace moe

@@ -82,6 +82,9 @@ struct GemmParams {
   const uint16_t *lora_w[MOE_LORA_MAX_SLOTS];  // SHRINK: A [E, r, K]; ext: B [E, N, r]
   int lora_w_shared;  // lora_w holds one matrix per slot for all experts (shared-outer)
   int w_packed;       // w is in the tile-packed layout (128-row x 64-column blocks)
+  // FP8 weights (kernels instantiated with W8): w holds E4M3 codes [E, N, K] (one byte
+  // each) and w_scale one fp32 scale per 128 x 128 block, [E, N/128, K/128]
+  const float *w_scale;
   const float *part;                            // ext A source [splits][R][rmax]
   int part_splits;
   // ext A source already reduced over the splits, scaled and rounded: bf16 [R][rmax]
@@ -104,9 +107,10 @@ struct GemmParams {
 // the 16-row tiles would fit the LDS but cap them at 168 VGPRs, where the four register
 // stages and the LoRA code spill to scratch on every tile (decode gate_up 155 -> 131 us
 // without the cap).
-template <int BM, int BN, int WM, int WN, int MODE, int PF>
+template <int BM, int BN, int WM, int WN, int MODE, int PF, bool W8 = false>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void moe_gemm_kernel(const GemmParams P) {
+  static_assert(!W8 || MODE == MODE_GATEUP || MODE == MODE_DOWN, "FP8 weights feed the gate_up and down GEMMs");
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -336,6 +340,24 @@ void moe_gemm_kernel(const GemmParams P) {
     // expert matrix is < 2 GiB (checked by the host), so both offsets fit 32 bits.
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(bbase), (short)0, 0x7fffffff, 0x00020000);
+    if constexpr (W8) {
+      // FP8 weights (row-major, bbase = the expert's first code byte): 8 codes per chunk
+      // into .xy, the chunk's block scale into .z; store_lds turns them into bf16
+      const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float *>(P.w_scale), (short)0, 0x7fffffff, 0x00020000);
+      const int KB = P.K / 128;
+#pragma unroll
+      for (int i = 0; i < B_IT; ++i) {
+        const int wr = (b_wrow[i] >= 0 && b_wrow[i] < bcount) ? b_wrow[i] : 0;
+        const uint32_t lo = (uint32_t)wr * (uint32_t)P.K + (uint32_t)b_c8[i] * 8u;
+        const auto v = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, lo, k0, decltype(nt)::value ? 2 : 0));
+        const uint32_t so = ((uint32_t)(e * (P.N / 128) + (wr >> 7)) * (uint32_t)KB) * 4u;
+        const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(ssrc, so, (k0 >> 7) * 4, 0);
+        xb[i] = u32x4_t{v.x, v.y, sc, 0u};
+      }
+      return;
+    }
     const int soff = decltype(pk)::value ? (k0 / BK) * P.N * BK * 2 : k0 * 2;
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
@@ -375,7 +397,21 @@ void moe_gemm_kernel(const GemmParams P) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) *reinterpret_cast<u32x4_t *>(&As[buf][a_lds[i]]) = xa[i];
 #pragma unroll
-    for (int i = 0; i < B_IT; ++i) *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = xb[i];
+    for (int i = 0; i < B_IT; ++i) {
+      if constexpr (W8) {
+        // 8 E4M3 codes (element j in byte j) -> fp32 (exact) * block scale -> bf16
+        const float sc = __uint_as_float(xb[i].z);
+        const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)xb[i].x, false);
+        const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)xb[i].x, true);
+        const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)xb[i].y, false);
+        const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)xb[i].y, true);
+        const u32x4_t o = {pack_bf16x2(f0.x * sc, f0.y * sc), pack_bf16x2(f1.x * sc, f1.y * sc),
+                           pack_bf16x2(f2.x * sc, f2.y * sc), pack_bf16x2(f3.x * sc, f3.y * sc)};
+        *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = o;
+      } else {
+        *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = xb[i];
+      }
+    }
   };
 
   // Fragment rows are 16-aligned bases plus (lane & 15), so the swizzle depends on the lane
@@ -616,7 +652,11 @@ void moe_gemm_kernel(const GemmParams P) {
           }
     }
   } else {
-    const uint16_t *wbase = kHasMain ? P.w + (size_t)e * P.N * P.K : nullptr;
+    // (FP8 weights: one byte per element, the pointer only carries the byte address)
+    const uint16_t *wbase =
+        !kHasMain ? nullptr
+        : W8 ? reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(P.w) + (size_t)e * P.N * P.K)
+             : P.w + (size_t)e * P.N * P.K;
     const int wcount = kGateUp ? 2 * P.I : P.N;
     zero_acc();
     // The expand's first batch of slots (up to PF, ascending).  When the K loop ends on a
@@ -1078,9 +1118,9 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, int PF>
+template <int BM, int BN, int WM, int WN, int MODE, int PF, bool W8 = false>
 int launch_cfg(const GemmParams &P, int n_cols, hipStream_t s) {
-  auto kernel = moe_gemm_kernel<BM, BN, WM, WN, MODE, PF>;
+  auto kernel = moe_gemm_kernel<BM, BN, WM, WN, MODE, PF, W8>;
   constexpr int threads = WM * WN * 64;
   int tiles = mtile_bound(P.R, P.E, BM);
   long long blocks = (long long)tiles * n_cols;
@@ -1108,14 +1148,14 @@ int launch_cfg(const GemmParams &P, int n_cols, hipStream_t s) {
 // n-tiles of the gate_up GEMM (each covers BN/2 intermediate columns)
 int gateup_ncols(int bm, int I) { return bm >= 128 ? cdiv(I, 128) : cdiv(I, 64); }
 
-template <int MODE>
+template <int MODE, bool W8 = false>
 int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
   const int BN = 128;
   const int ncols = (MODE == MODE_GATEUP) ? cdiv(P.I, BN / 2) : cdiv(P.N, BN);
   switch (bm) {
-    case 16: return launch_cfg<16, 128, 1, 4, MODE, 4>(P, ncols, s);
-    case 64: return launch_cfg<64, 128, 2, 2, MODE, 2>(P, ncols, s);
-    default: return launch_cfg<128, 256, 4, 2, MODE, 2>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
+    case 16: return launch_cfg<16, 128, 1, 4, MODE, 4, W8>(P, ncols, s);
+    case 64: return launch_cfg<64, 128, 2, 2, MODE, 2, W8>(P, ncols, s);
+    default: return launch_cfg<128, 256, 4, 2, MODE, 2, W8>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
   }
 }
 
@@ -1293,8 +1333,10 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
                    const int32_t *offsets, const int32_t *p2e, const uint16_t *w1,
                    const uint16_t *w2, const moe_lora_adapters *lora, uint16_t *y_perm, void *ws,
                    size_t ws_bytes, hipStream_t main, hipStream_t side,
-                   const moe_lora_options *opts) {
+                   const moe_lora_options *opts, const float *w1_scale, const float *w2_scale) {
   const int R = d.num_tokens * d.top_k;
+  // FP8 weights (w1/w2 hold E4M3 codes, block scales given): fused path only
+  const bool fp8 = w1_scale != nullptr;
   if (R == 0) return ST_OK;
   const FwdLayout L = layout(d, lora);
   if (ws_bytes < L.total) return ST_WS_SMALL;
@@ -1335,6 +1377,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   const bool decomposed =
       has_lora && L.decomposed && (force == 2 || (force == 0 && side && d.num_tokens <= two_max));
   if (force == 2 && has_lora && !L.decomposed) return ST_UNSUPPORTED;
+  if (fp8 && decomposed) return ST_UNSUPPORTED;
   // the side stream is used only by the decomposed path
   hipStream_t lora_stream = (decomposed && side) ? side : main;
 
@@ -1357,6 +1400,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   gu.K = d.hidden;
   gu.N = 2 * d.inter;
   gu.w_packed = packed & 1;
+  gu.w_scale = w1_scale;
 
   if (!decomposed) {
     // fused: shrink, then the GEMM appends the LoRA expand as extra K steps and applies
@@ -1374,7 +1418,9 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       gu.down_part = v_part;
     }
     if (ev0 && hipEventRecord(ev0, main) != hipSuccess) return ST_HIP;
-    if ((st = launch_gemm<MODE_GATEUP>(gu, bm, main)) != ST_OK) return st;
+    if ((st = fp8 ? launch_gemm<MODE_GATEUP, true>(gu, bm, main) : launch_gemm<MODE_GATEUP>(gu, bm, main)) !=
+        ST_OK)
+      return st;
     if (ev1 && hipEventRecord(ev1, main) != hipSuccess) return ST_HIP;
   } else {
     // decomposed: the LoRA shrink and expand (delta D) run on the side stream while main
@@ -1435,6 +1481,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     P.K = d.inter;
     P.N = d.hidden;
     P.w_packed = (packed >> 1) & 1;
+    P.w_scale = w2_scale;
     if (has_lora) {
       for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->b_down[s];
       P.lora_w_shared = lora->shared_outer;  // shared-outer: one B2 for all experts
@@ -1459,7 +1506,8 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       }
     }
     P.out_bf16 = y_perm;
-    if ((st = launch_gemm<MODE_DOWN>(P, bm, main)) != ST_OK) return st;
+    if ((st = fp8 ? launch_gemm<MODE_DOWN, true>(P, bm, main) : launch_gemm<MODE_DOWN>(P, bm, main)) != ST_OK)
+      return st;
   }
   return ST_OK;
 }

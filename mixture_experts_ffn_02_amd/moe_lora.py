@@ -113,6 +113,18 @@ def moe_lora_forward(d: Dims, x, x_perm, expert_offsets, p2e, w_gate_up, w_down,
         ctypes.byref(opts) if opts is not None else None))
 
 
+def moe_lora_forward_fp8(d: Dims, x, x_perm, expert_offsets, p2e, w_gate_up, w_gate_up_scale, w_down,
+                         w_down_scale, lora: Optional[Adapters], y_perm, ws, main=None, side=None,
+                         opts: Optional[Options] = None) -> None:
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    check("moe_lora_forward_fp8", load().moe_lora_forward_fp8(
+        ctypes.byref(d), _ptr(x), _ptr(x_perm), _ptr(expert_offsets), _ptr(p2e), _ptr(w_gate_up),
+        _ptr(w_gate_up_scale), _ptr(w_down), _ptr(w_down_scale),
+        ctypes.byref(lora) if lora is not None else None, _ptr(y_perm), _ptr(ws), ws_bytes,
+        _stream(main), None if side is None else _stream(side),
+        ctypes.byref(opts) if opts is not None else None))
+
+
 def moe_lora_pack_weights(d: Dims, w_gate_up, w_down, w_gate_up_packed, w_down_packed,
                           stream=None) -> None:
     check("moe_lora_pack_weights", load().moe_lora_pack_weights(
@@ -142,15 +154,25 @@ class MoELoRALayer:
     (PACKED_GATE_UP | PACKED_DOWN bits; True = both) makes the layer keep tile-packed
     copies of those expert weights (written once by moe_lora_pack_weights) and run the
     GEMMs on them; weights_prepacked gives the bits of the weights that are passed in
-    already packed.
+    already packed.  With w_gate_up_scale / w_down_scale the expert weights are FP8: uint8
+    E4M3 codes [E, 2I, H] / [E, H, I] with fp32 scales per 128 x 128 block, run through
+    moe_lora_forward_fp8 (row-major only).
     """
 
     def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int,
                  w_gate_up: torch.Tensor, w_down: torch.Tensor,
                  routing: int = ROUTING_RENORMALIZE, n_group: int = 1, topk_group: int = 1,
                  routed_scaling_factor: float = 1.0, correction_bias: Optional[torch.Tensor] = None,
-                 gather_on_load: bool = True, packed_weights=0, weights_prepacked=0):
+                 gather_on_load: bool = True, packed_weights=0, weights_prepacked=0,
+                 w_gate_up_scale: Optional[torch.Tensor] = None, w_down_scale: Optional[torch.Tensor] = None):
         load()
+        self.w_scales = None
+        if (w_gate_up_scale is None) != (w_down_scale is None):
+            raise ValueError("FP8 weights need both block-scale tensors")
+        if w_gate_up_scale is not None:
+            if packed_weights or weights_prepacked:
+                raise ValueError("FP8 weights run on the row-major layout only")
+            self.w_scales = (w_gate_up_scale, w_down_scale)
         self.H, self.I, self.E, self.k = hidden, inter, num_experts, top_k
         both = PACKED_GATE_UP | PACKED_DOWN
         to_pack = both if packed_weights is True else int(packed_weights)
@@ -221,8 +243,13 @@ class MoELoRALayer:
                 ctypes.memmove(ctypes.byref(o), ctypes.byref(opts), ctypes.sizeof(Options))
             o.packed_weights = self.packed_weights
             opts = o
-        moe_lora_forward(d, x, b["x_perm"], b["off"], b["p2e"], self.w_gate_up, self.w_down,
-                         c_lora, b["y"], b["fws"], stream, side_stream, opts)
+        if self.w_scales is not None:
+            moe_lora_forward_fp8(d, x, b["x_perm"], b["off"], b["p2e"], self.w_gate_up, self.w_scales[0],
+                                 self.w_down, self.w_scales[1], c_lora, b["y"], b["fws"], stream,
+                                 side_stream, opts)
+        else:
+            moe_lora_forward(d, x, b["x_perm"], b["off"], b["p2e"], self.w_gate_up, self.w_down,
+                             c_lora, b["y"], b["fws"], stream, side_stream, opts)
         moe_lora_finalize(d, b["y"], b["w"], b["e2p"], b["out"], stream)
         return b["out"]
 

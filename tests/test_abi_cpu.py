@@ -17,7 +17,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_lora_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_lora_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_and_binding_agree():
@@ -191,3 +191,24 @@ def test_pack_weights_argument_checks():
     assert lib.moe_lora_pack_weights(ctypes.byref(d), None, None, None, None, None) == _lib.ERR_INVALID_ARGUMENT
     # packing in place (overlapping source and destination) is rejected
     assert lib.moe_lora_pack_weights(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_forward_fp8_argument_checks():
+    lib = pkg.load()
+    d = _lib.Dims(16, 256, 128, 8, 2)
+    ws = 1 << 20
+
+    def call(dd, s1=FAKE, s2=FAKE, opts=None):
+        return lib.moe_lora_forward_fp8(ctypes.byref(dd), FAKE, None, FAKE, FAKE, FAKE, s1, FAKE, s2, None,
+                                        FAKE, FAKE, ws, None, None, ctypes.byref(opts) if opts else None)
+
+    assert call(d, s1=None) == _lib.ERR_INVALID_ARGUMENT
+    assert call(d, s2=FAKE + 4) == _lib.ERR_INVALID_ARGUMENT  # scales 16-byte aligned
+    assert call(_lib.Dims(16, 256, 192, 8, 2)) == _lib.ERR_UNSUPPORTED  # I % 128
+    assert call(_lib.Dims(16, 320, 128, 8, 2)) == _lib.ERR_UNSUPPORTED  # H % 128
+    o = _lib.Options()
+    o.packed_weights = 1
+    assert call(d, opts=o) == _lib.ERR_UNSUPPORTED
+    o = _lib.Options()
+    o.force_path = 2
+    assert call(d, opts=o) == _lib.ERR_UNSUPPORTED
