@@ -278,7 +278,7 @@ def main():
         c2, s2 = fp8_stack(wl.w_down_fp8)
         layer_fp8 = ml.MoELoRALayer(cfg.H, cfg.I, cfg.E, cfg.top_k, c1, c2, routing, cfg.n_group,
                                     cfg.topk_group, cfg.routed_scaling_factor, bias, gather_on_load=True,
-                                    w_gate_up_scale=s1, w_down_scale=s2)
+                                    packed_weights=packed, w_gate_up_scale=s1, w_down_scale=s2)
         t_fp8, fp8_gate_up_ms = timed(layer_fp8, lora, args.steps, args.warmup, gate_up_events=True)
         del layer_fp8, c1, c2, s1, s2
 
@@ -356,7 +356,8 @@ def main():
         "ms_per_step_row_major_weights": round(t_rm * 1e3, 4) if t_rm else None,
         "fp8_weights": None if t_fp8 is None else {
             "ms_per_step": round(t_fp8 * 1e3, 4), "value": round(T / t_fp8, 1), "unit": "tokens/s",
-            "weights": "E4M3 codes, fp32 scale per 128x128 block; LoRA bf16",
+            "weights": "E4M3 codes, fp32 scale per 128x128 block; LoRA bf16; codes "
+                       + ("tile-packed" if packed else "row-major"),
             "gate_up_us": round(fp8_gate_up_ms * 1e3, 2),
             "gate_up_algorithmic_bytes": int(gate_up_bytes_fp8),
             "gate_up_achieved_gbs": round(gate_up_bytes_fp8 / (fp8_gate_up_ms * 1e-3) / 1e9, 1),

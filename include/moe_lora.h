@@ -208,9 +208,11 @@ int moe_lora_forward(const moe_lora_dims *dims, const uint16_t *x, const uint16_
  * Each weight is rounded to bf16 once (fp32 product, round to nearest even) before the
  * bf16 MFMA; everything else is as in moe_lora_forward, whose workspace size applies.
  * All four weight pointers are device pointers, 16-byte aligned (else
- * MOE_LORA_ERR_INVALID_ARGUMENT).  Requires hidden % 128 == 0 and inter % 128 == 0, and
- * runs the fused path only: opts->packed_weights != 0 or opts->force_path == 2 ->
- * MOE_LORA_ERR_UNSUPPORTED; a side stream is not used. */
+ * MOE_LORA_ERR_INVALID_ARGUMENT).  Requires hidden and inter multiples of 128 and at most
+ * 8192, and
+ * runs the fused path only: opts->force_path == 2 -> MOE_LORA_ERR_UNSUPPORTED; a side
+ * stream is not used.  opts->packed_weights bits say which weights are in the FP8
+ * tile-packed layout of moe_lora_pack_weights_fp8 (the scales are never packed). */
 int moe_lora_forward_fp8(const moe_lora_dims *dims, const uint16_t *x, const uint16_t *x_perm,
                          const int32_t *expert_offsets, const int32_t *permuted_to_expanded,
                          const uint8_t *w_gate_up, const float *w_gate_up_scale,
@@ -237,6 +239,18 @@ int moe_lora_forward_fp8(const moe_lora_dims *dims, const uint16_t *x, const uin
 int moe_lora_pack_weights(const moe_lora_dims *dims, const uint16_t *w_gate_up, const uint16_t *w_down,
                           uint16_t *w_gate_up_packed, uint16_t *w_down_packed,
                           moe_lora_stream_t stream);
+
+/* ---------------------------------------------------------------- pack FP8 weights
+ * Tile-packed copies of FP8 expert weights for moe_lora_forward_fp8 (the LDS staging
+ * needs no change: only the codes' order in memory differs).  Same block order as
+ * moe_lora_pack_weights, each block 128 rows x 64 codes (8 KB, row-major), so a 64-wide
+ * K step of 128 output rows is one contiguous 8 KB read instead of 128 pieces of 64 bytes.
+ *   w_gate_up [E, 2I, H] -> w_gate_up_packed, w_down [E, H, I] -> w_down_packed, uint8
+ *   codes, device pointers, 16-byte aligned, not overlapping; a pair of two NULLs is
+ *   skipped (at least one pair is needed).  Requires hidden % 128 == 0 and
+ *   inter % 128 == 0 (else MOE_LORA_ERR_UNSUPPORTED).  Enqueued on `stream`. */
+int moe_lora_pack_weights_fp8(const moe_lora_dims *dims, const uint8_t *w_gate_up, const uint8_t *w_down,
+                              uint8_t *w_gate_up_packed, uint8_t *w_down_packed, moe_lora_stream_t stream);
 
 /* ---------------------------------------------------------------- finalize
  * out[t, :] = bf16( sum_j topk_weights[t, j] * y_perm[expanded_to_permuted[t*k+j], :] ),

@@ -38,6 +38,7 @@ EXPORTED = (
     "moe_lora_forward",
     "moe_lora_forward_fp8",
     "moe_lora_pack_weights",
+    "moe_lora_pack_weights_fp8",
     "moe_lora_finalize",
 )
 
@@ -114,6 +115,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_lora_pack_weights.restype = c_int
     lib.moe_lora_pack_weights.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
                                           c_void_p]
+    lib.moe_lora_pack_weights_fp8.restype = c_int
+    lib.moe_lora_pack_weights_fp8.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p]
     lib.moe_lora_finalize.restype = c_int
     lib.moe_lora_finalize.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p]

@@ -151,6 +151,26 @@ int moe_lora_pack_weights(const moe_lora_dims *d, const uint16_t *w_gate_up, con
                                   reinterpret_cast<hipStream_t>(stream));
 }
 
+int moe_lora_pack_weights_fp8(const moe_lora_dims *d, const uint8_t *w_gate_up, const uint8_t *w_down,
+                              uint8_t *w_gate_up_packed, uint8_t *w_down_packed, moe_lora_stream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_LORA_OK) return st;
+  if (d->hidden % 128 != 0 || d->inter % 128 != 0) return MOE_LORA_ERR_UNSUPPORTED;
+  const bool do1 = w_gate_up || w_gate_up_packed, do2 = w_down || w_down_packed;
+  if (!do1 && !do2) return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (do1 && (!w_gate_up || !w_gate_up_packed || !aligned16(w_gate_up) || !aligned16(w_gate_up_packed)))
+    return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (do2 && (!w_down || !w_down_packed || !aligned16(w_down) || !aligned16(w_down_packed)))
+    return MOE_LORA_ERR_INVALID_ARGUMENT;
+  const size_t n1 = (size_t)d->num_experts * 2 * d->inter * d->hidden, n2 = (size_t)d->num_experts * d->hidden * d->inter;
+  const uintptr_t a1 = reinterpret_cast<uintptr_t>(w_gate_up), b1 = reinterpret_cast<uintptr_t>(w_gate_up_packed);
+  const uintptr_t a2 = reinterpret_cast<uintptr_t>(w_down), b2 = reinterpret_cast<uintptr_t>(w_down_packed);
+  if ((do1 && a1 < b1 + n1 && b1 < a1 + n1) || (do2 && a2 < b2 + n2 && b2 < a2 + n2))
+    return MOE_LORA_ERR_INVALID_ARGUMENT;  // in-place packing is not supported
+  return moe::launch_pack_weights_fp8(*d, w_gate_up, w_down, w_gate_up_packed, w_down_packed,
+                                      reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t moe_lora_forward_workspace_size(const moe_lora_dims *d, const moe_lora_adapters *lora) {
   if (check_dims(d) != MOE_LORA_OK || check_lora_shape(lora) != MOE_LORA_OK) return 0;
   return moe::forward_workspace_size(*d, lora);
@@ -175,7 +195,8 @@ int forward_checked(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x
     return MOE_LORA_ERR_UNSUPPORTED;
   if (fp8) {
     if (d->hidden % 128 != 0 || d->inter % 128 != 0) return MOE_LORA_ERR_UNSUPPORTED;
-    if (opts && (opts->packed_weights || opts->force_path == 2)) return MOE_LORA_ERR_UNSUPPORTED;
+    if (d->hidden > 8192 || d->inter > 8192) return MOE_LORA_ERR_UNSUPPORTED;  // per-tile scale table
+    if (opts && opts->force_path == 2) return MOE_LORA_ERR_UNSUPPORTED;
   }
   if (d->num_tokens == 0) return MOE_LORA_OK;
   if (!x && !x_perm) return MOE_LORA_ERR_INVALID_ARGUMENT;

@@ -36,6 +36,8 @@ int launch_finalize(const uint16_t *y_perm, const float *w, const int32_t *e2p, 
                     int T, int H, int K, hipStream_t s);
 
 // ---- tile-packed expert weights ---------------------------------------------------
+int launch_pack_weights_fp8(const moe_lora_dims &d, const uint8_t *w1, const uint8_t *w2, uint8_t *w1p,
+                            uint8_t *w2p, hipStream_t s);
 int launch_pack_weights(const moe_lora_dims &d, const uint16_t *w1, const uint16_t *w2, uint16_t *w1p,
                         uint16_t *w2p, hipStream_t s);
 

@@ -115,6 +115,11 @@ void moe_gemm_kernel(const GemmParams P) {
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int A_CH = BM * (BK / 8), B_CH = BN * (BK / 8);
+  // FP8 weights: 16-byte chunks of 16 codes (two bf16 LDS chunks each)
+  constexpr int B8_CH = BN * (BK / 16), B8_IT = (B8_CH + WM * WN * 64 - 1) / (WM * WN * 64);
+  // slots whose expand B rows ride in the register stages at once (a deep FP8 pipeline
+  // would otherwise multiply those registers)
+  constexpr int EB = PF < 4 ? PF : 4;
   constexpr int A_IT = (A_CH + NT - 1) / NT, B_IT = (B_CH + NT - 1) / NT;
   constexpr bool kGateUp = (MODE == MODE_GATEUP);
   constexpr bool kHasMain = (MODE != MODE_EXPAND_F32);
@@ -140,6 +145,9 @@ void moe_gemm_kernel(const GemmParams P) {
   // per-lane a is a vector load from the argument block, which waits behind the weight
   // stream)
   __shared__ int s_rank[MOE_LORA_MAX_SLOTS];
+  // FP8 weights: the tile's block scales, [2 row blocks][K / 128 <= 64] (gate_up: the gate
+  // and the up block of the tile's columns; down: the tile's one or two row blocks)
+  __shared__ float s_wsc[W8 ? 2 * 64 : 1];
   // LoRA expand A operand of the tile: row r holds bf16(s_a * sum of shrink partials) over
   // the rank columns of its own slot (zero elsewhere); built once, masked per slot later
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kHasExt ? BM * BK : 8];
@@ -265,6 +273,14 @@ void moe_gemm_kernel(const GemmParams P) {
     s_slot[r] = slot;
     if (slot >= 0) atomicOr(&s_mask[parity], 1 << slot);
   }
+  if constexpr (W8) {
+    const int KB = P.K / 128, NB = P.N / 128;
+    for (int q = tid; q < 2 * KB; q += NT) {
+      const int j = q / KB, kb = q % KB;
+      const int rblk = kGateUp ? ((j ? P.I : 0) + col * (BN / 2)) / 128 : (col * BN) / 128 + j;
+      s_wsc[q] = rblk < NB ? P.w_scale[((size_t)e * NB + rblk) * KB + kb] : 0.f;
+    }
+  }
   __syncthreads();
   const int slot_mask = __builtin_amdgcn_readfirstlane(s_mask[parity]);
   // the expert's rows fit this one tile: its weight rows are read by no other block
@@ -313,7 +329,43 @@ void moe_gemm_kernel(const GemmParams P) {
     }
     // packed block (e, s, t) holds rows 128 t .. of the LDS order above for K step s
     b_pk[i] = 0;
-    if constexpr (BN % 128 == 0) b_pk[i] = ((col * (BN / 128) + n / 128) * 128 + n % 128) * BK + (cc & 7) * 8;
+    // (padding rows of a 256-wide tile past the last 128-row tile read tile 0 instead: their
+    // block would lie past the expert's region)
+    if constexpr (BN % 128 == 0) {
+      int tt = col * (BN / 128) + n / 128;
+      if (tt >= (kGateUp || MODE == MODE_GATEUP_F32 ? 2 * P.I : P.N) / 128) tt = 0;
+      b_pk[i] = (tt * 128 + n % 128) * BK + (cc & 7) * 8;
+    }
+  }
+
+  // FP8 main-loop chunks: byte offset (row, 16 columns) in the expert's code matrix at K
+  // step 0, the two LDS chunk offsets, and the chunk's scale row in s_wsc
+  uint32_t b8_lo[W8 ? B8_IT : 1], b8_pk[W8 ? B8_IT : 1];  // row-major / tile-packed codes
+  int b8_lds[W8 ? B8_IT : 1], b8_lds2[W8 ? B8_IT : 1], b8_sj[W8 ? B8_IT : 1];
+  if constexpr (W8) {
+#pragma unroll
+    for (int i = 0; i < B8_IT; ++i) {
+      const int c = tid + i * NT;
+      const int cc = c < B8_CH ? c : c % B8_CH;
+      const int n = cc >> 2, c16 = cc & 3;
+      int wr;
+      if constexpr (kGateUp) {
+        const int icol = col * (BN / 2) + (n / 128) * 64 + n % 64;  // see brow()
+        wr = icol < P.I ? ((n % 128) / 64) * P.I + icol : 0;
+        b8_sj[i] = (n % 128) / 64;
+      } else {
+        const int ng = col * BN + n;
+        wr = ng < P.N ? ng : 0;
+        b8_sj[i] = n / 128;
+      }
+      b8_lo[i] = (uint32_t)wr * (uint32_t)P.K + (uint32_t)c16 * 16u;
+      // packed: block (e, s, t) of 128 rows x 64 codes, t = the LDS row's 128-row tile
+      int tt = col * (BN / 128) + n / 128;
+      if (tt >= P.N / 128) tt = 0;  // padding rows past the last tile (see b_pk)
+      b8_pk[i] = (uint32_t)((tt * 128 + n % 128) * 64 + c16 * 16);
+      b8_lds[i] = lds_off(n, 2 * c16);
+      b8_lds2[i] = lds_off(n, 2 * c16 + 1);
+    }
   }
 
   u32x4_t ra[PF][A_IT], rb[PF][B_IT];
@@ -341,21 +393,15 @@ void moe_gemm_kernel(const GemmParams P) {
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(bbase), (short)0, 0x7fffffff, 0x00020000);
     if constexpr (W8) {
-      // FP8 weights (row-major, bbase = the expert's first code byte): 8 codes per chunk
-      // into .xy, the chunk's block scale into .z; store_lds turns them into bf16
-      const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float *>(P.w_scale), (short)0, 0x7fffffff, 0x00020000);
-      const int KB = P.K / 128;
+      // FP8 weights (row-major, bbase = the expert's first code byte): 16 codes per chunk;
+      // store_lds scales them into bf16
+      // (packed: the K step's blocks start k0 * N bytes into the expert's region)
+      const int soff8 = decltype(pk)::value ? k0 * P.N : k0;
 #pragma unroll
-      for (int i = 0; i < B_IT; ++i) {
-        const int wr = (b_wrow[i] >= 0 && b_wrow[i] < bcount) ? b_wrow[i] : 0;
-        const uint32_t lo = (uint32_t)wr * (uint32_t)P.K + (uint32_t)b_c8[i] * 8u;
-        const auto v = __builtin_bit_cast(
-            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, lo, k0, decltype(nt)::value ? 2 : 0));
-        const uint32_t so = ((uint32_t)(e * (P.N / 128) + (wr >> 7)) * (uint32_t)KB) * 4u;
-        const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(ssrc, so, (k0 >> 7) * 4, 0);
-        xb[i] = u32x4_t{v.x, v.y, sc, 0u};
-      }
+      for (int i = 0; i < B8_IT; ++i)
+        xb[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, decltype(pk)::value ? b8_pk[i] : b8_lo[i],
+                                                           soff8, decltype(nt)::value ? 2 : 0));
       return;
     }
     const int soff = decltype(pk)::value ? (k0 / BK) * P.N * BK * 2 : k0 * 2;
@@ -393,24 +439,33 @@ void moe_gemm_kernel(const GemmParams P) {
 
   // threads past the chunk count hold a duplicate of another thread's chunk, so every
   // thread stores unconditionally (identical values to the same address)
-  auto store_lds = [&](int buf, const u32x4_t(&xa)[A_IT], const u32x4_t(&xb)[B_IT]) {
+  // (step: the K step being stored, which picks the FP8 block scale)
+  auto store_lds = [&](int buf, const u32x4_t(&xa)[A_IT], const u32x4_t(&xb)[B_IT], int step) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) *reinterpret_cast<u32x4_t *>(&As[buf][a_lds[i]]) = xa[i];
+    if constexpr (W8) {
+      // 16 E4M3 codes (element j in byte j) -> fp32 (exact) * block scale -> bf16
+      const int kb = step >> 1, KB = P.K / 128;
 #pragma unroll
-    for (int i = 0; i < B_IT; ++i) {
-      if constexpr (W8) {
-        // 8 E4M3 codes (element j in byte j) -> fp32 (exact) * block scale -> bf16
-        const float sc = __uint_as_float(xb[i].z);
-        const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)xb[i].x, false);
-        const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)xb[i].x, true);
-        const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)xb[i].y, false);
-        const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)xb[i].y, true);
-        const u32x4_t o = {pack_bf16x2(f0.x * sc, f0.y * sc), pack_bf16x2(f1.x * sc, f1.y * sc),
-                           pack_bf16x2(f2.x * sc, f2.y * sc), pack_bf16x2(f3.x * sc, f3.y * sc)};
-        *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = o;
-      } else {
-        *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = xb[i];
+      for (int i = 0; i < B8_IT; ++i) {
+        const float sc = s_wsc[b8_sj[i] * KB + kb];
+        u32x4_t o[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int w0 = (int)xb[i][2 * h], w1 = (int)xb[i][2 * h + 1];
+          const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+          const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+          const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+          const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+          o[h] = u32x4_t{pack_bf16x2(f0.x * sc, f0.y * sc), pack_bf16x2(f1.x * sc, f1.y * sc),
+                         pack_bf16x2(f2.x * sc, f2.y * sc), pack_bf16x2(f3.x * sc, f3.y * sc)};
+        }
+        *reinterpret_cast<u32x4_t *>(&Bs[buf][b8_lds[i]]) = o[0];
+        *reinterpret_cast<u32x4_t *>(&Bs[buf][b8_lds2[i]]) = o[1];
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_IT; ++i) *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = xb[i];
     }
   };
 
@@ -583,14 +638,14 @@ void moe_gemm_kernel(const GemmParams P) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) load_full((s_begin + u) * BK, bbase, bcount, ra[u], rb[u], nt, pk);
       pre();
-      store_lds(0, ra[0], rb[0]);
+      store_lds(0, ra[0], rb[0], s_begin);
       __syncthreads();
       for (int i = 0; i < n_main - PF; i += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
           load_full((s_begin + i + u + PF) * BK, bbase, bcount, ra[u], rb[u], nt, pk);
           compute(u & 1);
-          store_lds((u + 1) & 1, ra[(u + 1) % PF], rb[(u + 1) % PF]);
+          store_lds((u + 1) & 1, ra[(u + 1) % PF], rb[(u + 1) % PF], s_begin + i + u + 1);
           __syncthreads();
         }
       }
@@ -598,7 +653,7 @@ void moe_gemm_kernel(const GemmParams P) {
       for (int u = 0; u < PF; ++u) {
         tail_load(u);
         compute(u & 1);
-        if (u + 1 < PF) store_lds((u + 1) & 1, ra[u + 1], rb[u + 1]);
+        if (u + 1 < PF) store_lds((u + 1) & 1, ra[u + 1], rb[u + 1], s_begin + n_main - PF + u + 1);
         __syncthreads();
       }
     } else {
@@ -606,7 +661,7 @@ void moe_gemm_kernel(const GemmParams P) {
     }
     for (int s = s_begin + n_main; s < s_end; ++s) {
       load_full(s * BK, bbase, bcount, ra[0], rb[0], nt, pk);
-      store_lds(0, ra[0], rb[0]);
+      store_lds(0, ra[0], rb[0], s);
       __syncthreads();
       compute(0);
       __syncthreads();
@@ -615,7 +670,7 @@ void moe_gemm_kernel(const GemmParams P) {
 
   auto run_single = [&](auto &&loader) {
     loader(ra[0], rb[0]);
-    store_lds(0, ra[0], rb[0]);
+    store_lds(0, ra[0], rb[0], 0);  // (K tails: never FP8, whose K is a multiple of 128)
     __syncthreads();
     compute(0);
     __syncthreads();
@@ -663,11 +718,11 @@ void moe_gemm_kernel(const GemmParams P) {
     // full pipelined step and those ranks are multiples of 8, their B operands are loaded
     // during the last PF main steps into the register stages those steps free, from
     // clamped addresses (no predicates), and masked when stored.
-    int batch0[PF];
+    int batch0[EB];
     int pending = slot_mask;
     bool r8 = true;
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int u = 0; u < EB; ++u) {
       batch0[u] = -1;
       if (pending) {
         batch0[u] = __ffs(pending) - 1;
@@ -791,7 +846,7 @@ void moe_gemm_kernel(const GemmParams P) {
     auto main_loop = [&](auto nt, auto pk) {
       if (kExtEarly && ext_early) {
         run_full(0, full, wbase, wcount, build, [&](int u) {
-          load_ext_b_clamped(batch0[u] >= 0 ? batch0[u] : batch0[0], rb[u]);
+          if (u < EB) load_ext_b_clamped(batch0[u] >= 0 ? batch0[u] : batch0[0], rb[u]);
         }, nt, pk);
       } else {
         run_full(0, full, wbase, wcount, build, [](int) {}, nt, pk);
@@ -846,9 +901,9 @@ void moe_gemm_kernel(const GemmParams P) {
       pending = slot_mask;
       bool first = true;
       while (pending) {
-        int batch[PF];
+        int batch[EB];
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
+        for (int u = 0; u < EB; ++u) {
           batch[u] = -1;
           if (pending) {
             batch[u] = __ffs(pending) - 1;
@@ -858,7 +913,7 @@ void moe_gemm_kernel(const GemmParams P) {
         if (first && ext_early) {
           // already in rb[]: zero the chunks outside B's rows and the slot's rank
 #pragma unroll
-          for (int u = 0; u < PF; ++u) {
+          for (int u = 0; u < EB; ++u) {
             if (batch[u] < 0) continue;
             const int ra_rank = P.rank[batch[u]];
 #pragma unroll
@@ -867,12 +922,12 @@ void moe_gemm_kernel(const GemmParams P) {
           }
         } else {
 #pragma unroll
-          for (int u = 0; u < PF; ++u)
+          for (int u = 0; u < EB; ++u)
             if (batch[u] >= 0) load_ext_b(batch[u], rb[u]);
         }
         first = false;
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
+        for (int u = 0; u < EB; ++u) {
           if (batch[u] < 0) continue;
           store_b(u & 1, rb[u]);
           __syncthreads();
@@ -1153,7 +1208,11 @@ int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
   const int BN = 128;
   const int ncols = (MODE == MODE_GATEUP) ? cdiv(P.I, BN / 2) : cdiv(P.N, BN);
   switch (bm) {
-    case 16: return launch_cfg<16, 128, 1, 4, MODE, 4, W8>(P, ncols, s);
+    // FP8 weights: a K step carries half the bytes, so the 16-row tiles keep more steps in
+    // flight (eight on gate_up, six on down; both divide the decode K of 2048 and 768)
+    case 16:
+      if constexpr (W8) return launch_cfg<16, 128, 1, 4, MODE, MODE == MODE_GATEUP ? 8 : 6, true>(P, ncols, s);
+      else return launch_cfg<16, 128, 1, 4, MODE, 4>(P, ncols, s);
     case 64: return launch_cfg<64, 128, 2, 2, MODE, 2, W8>(P, ncols, s);
     default: return launch_cfg<128, 256, 4, 2, MODE, 2, W8>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
   }

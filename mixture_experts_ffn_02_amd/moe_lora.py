@@ -132,6 +132,13 @@ def moe_lora_pack_weights(d: Dims, w_gate_up, w_down, w_gate_up_packed, w_down_p
         _stream(stream)))
 
 
+def moe_lora_pack_weights_fp8(d: Dims, w_gate_up, w_down, w_gate_up_packed, w_down_packed,
+                              stream=None) -> None:
+    check("moe_lora_pack_weights_fp8", load().moe_lora_pack_weights_fp8(
+        ctypes.byref(d), _ptr(w_gate_up), _ptr(w_down), _ptr(w_gate_up_packed), _ptr(w_down_packed),
+        _stream(stream)))
+
+
 def moe_lora_finalize(d: Dims, y_perm, topk_weights, e2p, out, stream=None) -> None:
     check("moe_lora_finalize", load().moe_lora_finalize(
         ctypes.byref(d), _ptr(y_perm), _ptr(topk_weights), _ptr(e2p), _ptr(out), _stream(stream)))
@@ -156,7 +163,8 @@ class MoELoRALayer:
     GEMMs on them; weights_prepacked gives the bits of the weights that are passed in
     already packed.  With w_gate_up_scale / w_down_scale the expert weights are FP8: uint8
     E4M3 codes [E, 2I, H] / [E, H, I] with fp32 scales per 128 x 128 block, run through
-    moe_lora_forward_fp8 (row-major only).
+    moe_lora_forward_fp8 (packed_weights / weights_prepacked then refer to the FP8
+    tile-packed layout of moe_lora_pack_weights_fp8).
     """
 
     def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int,
@@ -170,8 +178,6 @@ class MoELoRALayer:
         if (w_gate_up_scale is None) != (w_down_scale is None):
             raise ValueError("FP8 weights need both block-scale tensors")
         if w_gate_up_scale is not None:
-            if packed_weights or weights_prepacked:
-                raise ValueError("FP8 weights run on the row-major layout only")
             self.w_scales = (w_gate_up_scale, w_down_scale)
         self.H, self.I, self.E, self.k = hidden, inter, num_experts, top_k
         both = PACKED_GATE_UP | PACKED_DOWN
@@ -183,8 +189,9 @@ class MoELoRALayer:
         if to_pack:
             w1p = torch.empty_like(w_gate_up) if to_pack & PACKED_GATE_UP else None
             w2p = torch.empty_like(w_down) if to_pack & PACKED_DOWN else None
-            moe_lora_pack_weights(self.dims(0), w_gate_up if w1p is not None else None,
-                                  w_down if w2p is not None else None, w1p, w2p)
+            pack = moe_lora_pack_weights_fp8 if self.w_scales is not None else moe_lora_pack_weights
+            pack(self.dims(0), w_gate_up if w1p is not None else None, w_down if w2p is not None else None,
+                 w1p, w2p)
             w_gate_up = w1p if w1p is not None else w_gate_up
             w_down = w2p if w2p is not None else w_down
         self.packed_weights = to_pack | pre

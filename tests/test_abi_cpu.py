@@ -206,9 +206,24 @@ def test_forward_fp8_argument_checks():
     assert call(d, s2=FAKE + 4) == _lib.ERR_INVALID_ARGUMENT  # scales 16-byte aligned
     assert call(_lib.Dims(16, 256, 192, 8, 2)) == _lib.ERR_UNSUPPORTED  # I % 128
     assert call(_lib.Dims(16, 320, 128, 8, 2)) == _lib.ERR_UNSUPPORTED  # H % 128
+    assert call(_lib.Dims(16, 8320, 128, 8, 2)) == _lib.ERR_UNSUPPORTED  # H > 8192
     o = _lib.Options()
-    o.packed_weights = 1
-    assert call(d, opts=o) == _lib.ERR_UNSUPPORTED
+    o.packed_weights = 4
+    assert call(d, opts=o) == _lib.ERR_INVALID_ARGUMENT
     o = _lib.Options()
     o.force_path = 2
     assert call(d, opts=o) == _lib.ERR_UNSUPPORTED
+
+
+def test_pack_weights_fp8_argument_checks():
+    lib = pkg.load()
+    d = _lib.Dims(16, 256, 128, 8, 2)
+    assert lib.moe_lora_pack_weights_fp8(ctypes.byref(d), None, None, None, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+    assert lib.moe_lora_pack_weights_fp8(ctypes.byref(d), FAKE, None, None, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT  # a pair needs both pointers
+    assert lib.moe_lora_pack_weights_fp8(ctypes.byref(d), FAKE, None, FAKE, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT  # in place
+    d2 = _lib.Dims(16, 256, 192, 8, 2)
+    assert lib.moe_lora_pack_weights_fp8(ctypes.byref(d2), FAKE, None, FAKE * 4, None, None) == \
+        _lib.ERR_UNSUPPORTED  # I % 128

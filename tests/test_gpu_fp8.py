@@ -48,16 +48,16 @@ class Fp8Case:
             self.dq2[e] = oracle.fp8_block_weights(self.c2[e], self.s2[e])
         return self.dq2[e]
 
-    def layer(self):
+    def layer(self, packed=0):
         c, g = self.cfg, self.g
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev())
         return ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, t(self.c1), t(self.c2), g.routing, c.n_group,
-                               c.topk_group, c.routed_scaling_factor, g.bias,
+                               c.topk_group, c.routed_scaling_factor, g.bias, packed_weights=packed,
                                w_gate_up_scale=t(self.s1), w_down_scale=t(self.s2))
 
-    def run(self, with_lora=True):
+    def run(self, with_lora=True, packed=0):
         g = self.g
-        out = self.layer()(g.x, g.logits, g.lora_slots() if with_lora else None)
+        out = self.layer(packed)(g.x, g.logits, g.lora_slots() if with_lora else None)
         torch.cuda.synchronize()
         return out.clone()
 
@@ -101,3 +101,14 @@ def test_fp8_pow2_scales_bit_identical_to_bf16_kernels(cfg):
     out16 = layer16(g.x, g.logits, g.lora_slots())
     torch.cuda.synchronize()
     assert torch.equal(out8, out16)
+
+
+@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], MID8, TALL8],
+                         ids=["tiny", "decode", "mid-64row", "tall-128row"])
+def test_fp8_packed_layouts_bit_identical(cfg):
+    """The FP8 tile-packed layout (each weight alone and both) only reorders the codes."""
+    say(f"[fp8 packed] {cfg.name}")
+    case = Fp8Case(cfg)
+    ref = case.run()
+    for packed in (ml.PACKED_GATE_UP, ml.PACKED_DOWN, ml.PACKED_GATE_UP | ml.PACKED_DOWN):
+        assert torch.equal(case.run(packed=packed), ref), packed
