@@ -257,7 +257,7 @@ def main():
         t_graph = (time.perf_counter() - t0) / args.steps
         del graph
 
-    t_fp8, fp8_gate_up_ms = None, None
+    t_fp8, fp8_gate_up_ms, t_fp8_p2 = None, None, None
     fp8_ok = cfg.H % 128 == 0 and cfg.I % 128 == 0 and cfg.E * 3 * cfg.I * cfg.H <= (1 << 31)
     if fp8_ok:
         log("timing LoRA on with FP8 expert weights (E4M3 codes, fp32 scale per 128x128 block)")
@@ -280,7 +280,15 @@ def main():
                                     cfg.topk_group, cfg.routed_scaling_factor, bias, gather_on_load=True,
                                     packed_weights=packed, w_gate_up_scale=s1, w_down_scale=s2)
         t_fp8, fp8_gate_up_ms = timed(layer_fp8, lora, args.steps, args.warmup, gate_up_events=True)
-        del layer_fp8, c1, c2, s1, s2
+        # power-of-two block scales with the fused scaled conversion (opts.fp8_pow2_scales)
+        p1 = fp8_stack(lambda e: wl.w_gate_up_fp8(e, pow2=True))[1]
+        p2 = fp8_stack(lambda e: wl.w_down_fp8(e, pow2=True))[1]
+        layer_p2 = ml.MoELoRALayer(cfg.H, cfg.I, cfg.E, cfg.top_k, layer_fp8.w_gate_up, layer_fp8.w_down,
+                                   routing, cfg.n_group, cfg.topk_group, cfg.routed_scaling_factor, bias,
+                                   gather_on_load=True, weights_prepacked=packed, w_gate_up_scale=p1,
+                                   w_down_scale=p2, fp8_pow2_scales=True)
+        t_fp8_p2, _ = timed(layer_p2, lora, max(5, args.steps // 2), args.warmup)
+        del layer_fp8, layer_p2, c1, c2, s1, s2, p1, p2
 
     # realized routing -> algorithmic bytes and flops
     layer(x, logits, lora)
@@ -361,7 +369,8 @@ def main():
             "gate_up_us": round(fp8_gate_up_ms * 1e3, 2),
             "gate_up_algorithmic_bytes": int(gate_up_bytes_fp8),
             "gate_up_achieved_gbs": round(gate_up_bytes_fp8 / (fp8_gate_up_ms * 1e-3) / 1e9, 1),
-            "gate_up_hbm_frac": round(gate_up_bytes_fp8 / (fp8_gate_up_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "gate_up_hbm_frac": round(gate_up_bytes_fp8 / (fp8_gate_up_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_per_step_pow2_scales": round(t_fp8_p2 * 1e3, 4)},
         "shared_outer": ({"ms_per_step": round(t_shared * 1e3, 4), "value": round(T / t_shared, 1),
                           "lora_ratio": round(t_off / t_shared, 4)} if t_shared else None),
         "layer_roofline": {

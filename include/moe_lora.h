@@ -121,7 +121,14 @@ typedef struct {
    * hidden % 128 == 0 and inter % 64 == 0 (else MOE_LORA_ERR_UNSUPPORTED); values
    * outside 0..3 -> MOE_LORA_ERR_INVALID_ARGUMENT. */
   int32_t packed_weights;
-  int32_t reserved[3];
+  /* moe_lora_forward_fp8 only: 1 = every block scale is a power of two (as in E8M0 /
+   * MX-style scaling), which lets the staging use gfx950's fused scaled FP8 -> bf16
+   * conversion (it applies only the scale's exponent); the result is then identical to
+   * the general path.  0 = arbitrary fp32 scales.  Other values ->
+   * MOE_LORA_ERR_INVALID_ARGUMENT; a scale that is not a power of two with 1 set gives
+   * wrong weights (the library does not read the scales on the host). */
+  int32_t fp8_pow2_scales;
+  int32_t reserved[2];
 } moe_lora_options;
 
 /* Human-readable name of a status code (static storage). */

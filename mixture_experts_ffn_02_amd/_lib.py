@@ -64,7 +64,8 @@ class Adapters(ctypes.Structure):
 class Options(ctypes.Structure):
     _fields_ = [("two_stream_max_tokens", c_int32), ("force_path", c_int32),
                 ("gate_up_event_begin", c_void_p), ("gate_up_event_end", c_void_p),
-                ("packed_weights", c_int32), ("reserved", c_int32 * 3)]
+                ("packed_weights", c_int32), ("fp8_pow2_scales", c_int32),
+                ("reserved", c_int32 * 2)]
 
 
 class MoELoRAError(RuntimeError):

@@ -191,6 +191,7 @@ int forward_checked(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x
   if ((st = check_lora(lora)) != MOE_LORA_OK) return st;
   if (opts && (opts->force_path < 0 || opts->force_path > 2)) return MOE_LORA_ERR_INVALID_ARGUMENT;
   if (opts && (opts->packed_weights < 0 || opts->packed_weights > 3)) return MOE_LORA_ERR_INVALID_ARGUMENT;
+  if (opts && (opts->fp8_pow2_scales < 0 || opts->fp8_pow2_scales > 1)) return MOE_LORA_ERR_INVALID_ARGUMENT;
   if (opts && opts->packed_weights && (d->hidden % 128 != 0 || d->inter % 64 != 0))
     return MOE_LORA_ERR_UNSUPPORTED;
   if (fp8) {

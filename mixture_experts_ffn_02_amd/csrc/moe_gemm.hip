@@ -82,8 +82,9 @@ struct GemmParams {
   const uint16_t *lora_w[MOE_LORA_MAX_SLOTS];  // SHRINK: A [E, r, K]; ext: B [E, N, r]
   int lora_w_shared;  // lora_w holds one matrix per slot for all experts (shared-outer)
   int w_packed;       // w is in the tile-packed layout (128-row x 64-column blocks)
-  // FP8 weights (kernels instantiated with W8): w holds E4M3 codes [E, N, K] (one byte
-  // each) and w_scale one fp32 scale per 128 x 128 block, [E, N/128, K/128]
+  // FP8 weights (kernels instantiated with W8 = 1, or 2 when every block scale is a power
+  // of two): w holds E4M3 codes [E, N, K] (one byte each) and w_scale one fp32 scale per
+  // 128 x 128 block, [E, N/128, K/128]
   const float *w_scale;
   const float *part;                            // ext A source [splits][R][rmax]
   int part_splits;
@@ -107,7 +108,7 @@ struct GemmParams {
 // the 16-row tiles would fit the LDS but cap them at 168 VGPRs, where the four register
 // stages and the LoRA code spill to scratch on every tile (decode gate_up 155 -> 131 us
 // without the cap).
-template <int BM, int BN, int WM, int WN, int MODE, int PF, bool W8 = false>
+template <int BM, int BN, int WM, int WN, int MODE, int PF, int W8 = 0>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void moe_gemm_kernel(const GemmParams P) {
   static_assert(!W8 || MODE == MODE_GATEUP || MODE == MODE_DOWN, "FP8 weights feed the gate_up and down GEMMs");
@@ -446,22 +447,41 @@ void moe_gemm_kernel(const GemmParams P) {
     if constexpr (W8) {
       // 16 E4M3 codes (element j in byte j) -> fp32 (exact) * block scale -> bf16
       const int kb = step >> 1, KB = P.K / 128;
+      if constexpr (W8 == 2) {
+        // power-of-two scales: one fused scaled conversion per two codes (exact)
 #pragma unroll
-      for (int i = 0; i < B8_IT; ++i) {
-        const float sc = s_wsc[b8_sj[i] * KB + kb];
-        u32x4_t o[2];
+        for (int i = 0; i < B8_IT; ++i) {
+          const float sc = s_wsc[b8_sj[i] * KB + kb];
+          u32x4_t o[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int w0 = (int)xb[i][2 * h], w1 = (int)xb[i][2 * h + 1];
-          const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
-          const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
-          const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
-          const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
-          o[h] = u32x4_t{pack_bf16x2(f0.x * sc, f0.y * sc), pack_bf16x2(f1.x * sc, f1.y * sc),
-                         pack_bf16x2(f2.x * sc, f2.y * sc), pack_bf16x2(f3.x * sc, f3.y * sc)};
+          for (int h = 0; h < 2; ++h) {
+            const int w0 = (int)xb[i][2 * h], w1 = (int)xb[i][2 * h + 1];
+            o[h] = u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true))};
+          }
+          *reinterpret_cast<u32x4_t *>(&Bs[buf][b8_lds[i]]) = o[0];
+          *reinterpret_cast<u32x4_t *>(&Bs[buf][b8_lds2[i]]) = o[1];
         }
-        *reinterpret_cast<u32x4_t *>(&Bs[buf][b8_lds[i]]) = o[0];
-        *reinterpret_cast<u32x4_t *>(&Bs[buf][b8_lds2[i]]) = o[1];
+      } else {
+#pragma unroll
+        for (int i = 0; i < B8_IT; ++i) {
+          const float sc = s_wsc[b8_sj[i] * KB + kb];
+          u32x4_t o[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int w0 = (int)xb[i][2 * h], w1 = (int)xb[i][2 * h + 1];
+            const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+            const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+            const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+            const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+            o[h] = u32x4_t{pack_bf16x2(f0.x * sc, f0.y * sc), pack_bf16x2(f1.x * sc, f1.y * sc),
+                           pack_bf16x2(f2.x * sc, f2.y * sc), pack_bf16x2(f3.x * sc, f3.y * sc)};
+          }
+          *reinterpret_cast<u32x4_t *>(&Bs[buf][b8_lds[i]]) = o[0];
+          *reinterpret_cast<u32x4_t *>(&Bs[buf][b8_lds2[i]]) = o[1];
+        }
       }
     } else {
 #pragma unroll
@@ -1173,7 +1193,7 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, int PF, bool W8 = false>
+template <int BM, int BN, int WM, int WN, int MODE, int PF, int W8 = 0>
 int launch_cfg(const GemmParams &P, int n_cols, hipStream_t s) {
   auto kernel = moe_gemm_kernel<BM, BN, WM, WN, MODE, PF, W8>;
   constexpr int threads = WM * WN * 64;
@@ -1203,15 +1223,16 @@ int launch_cfg(const GemmParams &P, int n_cols, hipStream_t s) {
 // n-tiles of the gate_up GEMM (each covers BN/2 intermediate columns)
 int gateup_ncols(int bm, int I) { return bm >= 128 ? cdiv(I, 128) : cdiv(I, 64); }
 
-template <int MODE, bool W8 = false>
+template <int MODE, int W8 = 0>
 int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
   const int BN = 128;
   const int ncols = (MODE == MODE_GATEUP) ? cdiv(P.I, BN / 2) : cdiv(P.N, BN);
   switch (bm) {
-    // FP8 weights: a K step carries half the bytes, so the 16-row tiles keep more steps in
-    // flight (eight on gate_up, six on down; both divide the decode K of 2048 and 768)
+    // FP8 weights: a K step carries half the bytes, so the down tiles keep six steps in
+    // flight; gate_up keeps four, where more stages measured slower (the conversion of
+    // the codes, not the loads, sets its pace); both divide the decode K of 2048 and 768
     case 16:
-      if constexpr (W8) return launch_cfg<16, 128, 1, 4, MODE, MODE == MODE_GATEUP ? 8 : 6, true>(P, ncols, s);
+      if constexpr (W8) return launch_cfg<16, 128, 1, 4, MODE, MODE == MODE_GATEUP ? 4 : 6, W8>(P, ncols, s);
       else return launch_cfg<16, 128, 1, 4, MODE, 4>(P, ncols, s);
     case 64: return launch_cfg<64, 128, 2, 2, MODE, 2, W8>(P, ncols, s);
     default: return launch_cfg<128, 256, 4, 2, MODE, 2, W8>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
@@ -1396,6 +1417,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   const int R = d.num_tokens * d.top_k;
   // FP8 weights (w1/w2 hold E4M3 codes, block scales given): fused path only
   const bool fp8 = w1_scale != nullptr;
+  const bool pow2 = fp8 && opts && opts->fp8_pow2_scales;  // power-of-two block scales
   if (R == 0) return ST_OK;
   const FwdLayout L = layout(d, lora);
   if (ws_bytes < L.total) return ST_WS_SMALL;
@@ -1477,7 +1499,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       gu.down_part = v_part;
     }
     if (ev0 && hipEventRecord(ev0, main) != hipSuccess) return ST_HIP;
-    if ((st = fp8 ? launch_gemm<MODE_GATEUP, true>(gu, bm, main) : launch_gemm<MODE_GATEUP>(gu, bm, main)) !=
+    if ((st = fp8 ? (pow2 ? launch_gemm<MODE_GATEUP, 2>(gu, bm, main) : launch_gemm<MODE_GATEUP, 1>(gu, bm, main)) : launch_gemm<MODE_GATEUP>(gu, bm, main)) !=
         ST_OK)
       return st;
     if (ev1 && hipEventRecord(ev1, main) != hipSuccess) return ST_HIP;
@@ -1565,7 +1587,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       }
     }
     P.out_bf16 = y_perm;
-    if ((st = fp8 ? launch_gemm<MODE_DOWN, true>(P, bm, main) : launch_gemm<MODE_DOWN>(P, bm, main)) != ST_OK)
+    if ((st = fp8 ? (pow2 ? launch_gemm<MODE_DOWN, 2>(P, bm, main) : launch_gemm<MODE_DOWN, 1>(P, bm, main)) : launch_gemm<MODE_DOWN>(P, bm, main)) != ST_OK)
       return st;
   }
   return ST_OK;

@@ -172,13 +172,15 @@ class MoELoRALayer:
                  routing: int = ROUTING_RENORMALIZE, n_group: int = 1, topk_group: int = 1,
                  routed_scaling_factor: float = 1.0, correction_bias: Optional[torch.Tensor] = None,
                  gather_on_load: bool = True, packed_weights=0, weights_prepacked=0,
-                 w_gate_up_scale: Optional[torch.Tensor] = None, w_down_scale: Optional[torch.Tensor] = None):
+                 w_gate_up_scale: Optional[torch.Tensor] = None, w_down_scale: Optional[torch.Tensor] = None,
+                 fp8_pow2_scales: bool = False):
         load()
         self.w_scales = None
         if (w_gate_up_scale is None) != (w_down_scale is None):
             raise ValueError("FP8 weights need both block-scale tensors")
         if w_gate_up_scale is not None:
             self.w_scales = (w_gate_up_scale, w_down_scale)
+        self.fp8_pow2_scales = bool(fp8_pow2_scales) and self.w_scales is not None
         self.H, self.I, self.E, self.k = hidden, inter, num_experts, top_k
         both = PACKED_GATE_UP | PACKED_DOWN
         to_pack = both if packed_weights is True else int(packed_weights)
@@ -244,11 +246,12 @@ class MoELoRALayer:
                        self.routing, self.grouped, stream)
         if not self.gather_on_load:
             moe_lora_permute(d, x, b["p2e"], b["x_perm"], stream)
-        if self.packed_weights:
+        if self.packed_weights or self.fp8_pow2_scales:
             o = Options()
             if opts is not None:
                 ctypes.memmove(ctypes.byref(o), ctypes.byref(opts), ctypes.sizeof(Options))
             o.packed_weights = self.packed_weights
+            o.fp8_pow2_scales = int(self.fp8_pow2_scales)
             opts = o
         if self.w_scales is not None:
             moe_lora_forward_fp8(d, x, b["x_perm"], b["off"], b["p2e"], self.w_gate_up, self.w_scales[0],

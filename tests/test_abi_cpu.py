@@ -211,6 +211,9 @@ def test_forward_fp8_argument_checks():
     o.packed_weights = 4
     assert call(d, opts=o) == _lib.ERR_INVALID_ARGUMENT
     o = _lib.Options()
+    o.fp8_pow2_scales = 2
+    assert call(d, opts=o) == _lib.ERR_INVALID_ARGUMENT
+    o = _lib.Options()
     o.force_path = 2
     assert call(d, opts=o) == _lib.ERR_UNSUPPORTED
 

@@ -48,16 +48,17 @@ class Fp8Case:
             self.dq2[e] = oracle.fp8_block_weights(self.c2[e], self.s2[e])
         return self.dq2[e]
 
-    def layer(self, packed=0):
+    def layer(self, packed=0, pow2_path=False):
         c, g = self.cfg, self.g
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev())
         return ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, t(self.c1), t(self.c2), g.routing, c.n_group,
                                c.topk_group, c.routed_scaling_factor, g.bias, packed_weights=packed,
-                               w_gate_up_scale=t(self.s1), w_down_scale=t(self.s2))
+                               w_gate_up_scale=t(self.s1), w_down_scale=t(self.s2),
+                               fp8_pow2_scales=pow2_path)
 
-    def run(self, with_lora=True, packed=0):
+    def run(self, with_lora=True, packed=0, pow2_path=False):
         g = self.g
-        out = self.layer(packed)(g.x, g.logits, g.lora_slots() if with_lora else None)
+        out = self.layer(packed, pow2_path)(g.x, g.logits, g.lora_slots() if with_lora else None)
         torch.cuda.synchronize()
         return out.clone()
 
@@ -94,6 +95,8 @@ def test_fp8_pow2_scales_bit_identical_to_bf16_kernels(cfg):
     say(f"[fp8 vs bf16] {cfg.name}")
     case = Fp8Case(cfg, pow2=True)
     out8 = case.run()
+    # the fused scaled conversion (opts.fp8_pow2_scales) gives the same bits
+    assert torch.equal(case.run(pow2_path=True, packed=ml.PACKED_GATE_UP | ml.PACKED_DOWN), out8)
     c, g = case.cfg, case.g
     layer16 = ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, _bf16_from_dequant(case, 1),
                               _bf16_from_dequant(case, 2), g.routing, c.n_group, c.topk_group,
