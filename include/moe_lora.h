@@ -154,8 +154,11 @@ int moe_lora_version(void);
  * Batches of up to 64 tokens take one launch; larger ones take two (per-block counts,
  * then final positions).
  * grouped must be non-NULL for MOE_LORA_ROUTING_DEEPSEEK_V3 and is ignored otherwise.
- * num_tokens above 256 * min(256, 32768 / E) (65536 for E = 128) returns
- * MOE_LORA_ERR_UNSUPPORTED (route such batches in chunks). */
+ * A batch runs on at most 256 workgroups of at most min(256, 32768 / E) tokens each, fewer
+ * where the method's LDS footprint (DeepSeek-V3 keeps fp64 keys) would pass 160 KiB;
+ * num_tokens above that limit returns MOE_LORA_ERR_UNSUPPORTED (route such batches in
+ * chunks).  Limits: 65536 tokens for E = 128, 32768 for E = 256, 16384 for E = 512 with
+ * Renormalize and 14848 with DeepSeek-V3 at k = 8. */
 size_t moe_lora_route_workspace_size(const moe_lora_dims *dims);
 int moe_lora_route(const moe_lora_dims *dims, int routing, const moe_lora_grouped *grouped,
                    const uint16_t *logits, int32_t *topk_ids, float *topk_weights,

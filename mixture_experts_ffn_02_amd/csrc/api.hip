@@ -68,7 +68,7 @@ int moe_lora_version(void) { return 1; }
 
 size_t moe_lora_route_workspace_size(const moe_lora_dims *d) {
   if (check_dims(d) != MOE_LORA_OK || d->num_tokens == 0) return 0;
-  return moe::route_workspace_bytes(d->num_tokens, d->num_experts);
+  return moe::route_workspace_bytes(d->num_tokens, d->num_experts, d->top_k);
 }
 
 int moe_lora_route(const moe_lora_dims *d, int routing, const moe_lora_grouped *g,
@@ -80,7 +80,8 @@ int moe_lora_route(const moe_lora_dims *d, int routing, const moe_lora_grouped *
   if (routing != MOE_LORA_ROUTING_RENORMALIZE && routing != MOE_LORA_ROUTING_DEEPSEEK_V3)
     return MOE_LORA_ERR_INVALID_ARGUMENT;
   const int E = d->num_experts, K = d->top_k;
-  if (d->num_tokens > moe::route_max_tokens(E)) return MOE_LORA_ERR_UNSUPPORTED;
+  if (d->num_tokens > moe::route_max_tokens(E, K, routing == MOE_LORA_ROUTING_DEEPSEEK_V3))
+    return MOE_LORA_ERR_UNSUPPORTED;
   moe::RouteArgs a{};
   if (routing == MOE_LORA_ROUTING_DEEPSEEK_V3) {
     if (!g) return MOE_LORA_ERR_INVALID_ARGUMENT;

@@ -24,8 +24,8 @@ struct RouteArgs {
   int32_t *p2e;
   int32_t *hist;  // workspace [num_wg][E]
 };
-size_t route_workspace_bytes(int T, int E);
-int route_max_tokens(int E);
+size_t route_workspace_bytes(int T, int E, int K);
+int route_max_tokens(int E, int K, bool dsv3);
 int launch_route(const RouteArgs &a, hipStream_t s);
 int launch_zero_offsets(int32_t *offsets, int E, hipStream_t s);
 

@@ -1455,10 +1455,11 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   const int packed = opts ? opts->packed_weights : 0;  // bit 0 W1, bit 1 W2 (validated by the API)
   int two_max = (opts && opts->two_stream_max_tokens > 0) ? opts->two_stream_max_tokens : kTwoStreamMaxT;
   if (two_max > kTwoStreamMaxT) two_max = kTwoStreamMaxT;
-  const bool decomposed =
-      has_lora && L.decomposed && (force == 2 || (force == 0 && side && d.num_tokens <= two_max));
+  // (FP8 weights run the fused path only and leave a side stream unused; a forced
+  // decomposed path was rejected by the API)
+  const bool decomposed = !fp8 && has_lora && L.decomposed &&
+                          (force == 2 || (force == 0 && side && d.num_tokens <= two_max));
   if (force == 2 && has_lora && !L.decomposed) return ST_UNSUPPORTED;
-  if (fp8 && decomposed) return ST_UNSUPPORTED;
   // the side stream is used only by the decomposed path
   hipStream_t lora_stream = (decomposed && side) ? side : main;
 

@@ -494,15 +494,23 @@ bool allow_lds(size_t lds) {
   return true;
 }
 
-// tokens per workgroup: bounded by the LDS copy of the logits block (64 KiB) and the id
-// buffer; DeepSeek-V3 tokens are heavier, so they are spread thinner
-int max_tok_per_wg(int E) {
-  const int m = 32768 / E;
-  return m < kMaxTokPerWg ? m : kMaxTokPerWg;
+constexpr size_t kRouteLdsMax = 160 * 1024;  // LDS of one gfx950 workgroup
+
+// tokens per workgroup: bounded by the LDS copy of the logits block (64 KiB), the id
+// buffer, and the whole LDS footprint of the method (the fp64 DeepSeek-V3 key rows take
+// 16 * E * 8 bytes: at E = 512 and k = 8 only 58 tokens fit beside them)
+int max_tok_per_wg(int E, int K, bool dsv3) {
+  int m = 32768 / E;
+  if (m > kMaxTokPerWg) m = kMaxTokPerWg;
+  const size_t fixed = route_lds_bytes(E, K, 0, dsv3) + 16;  // + 16: the alignment pad
+  const size_t per_tok = (size_t)K * 4 + (size_t)E * sizeof(uint16_t);
+  const int fit = fixed < kRouteLdsMax ? (int)((kRouteLdsMax - fixed) / per_tok) : 0;
+  return m < fit ? m : fit;
 }
 
-int plan_route(int T, int E, bool dsv3, int &tok_per_wg) {
-  const int mx = max_tok_per_wg(E);
+int plan_route(int T, int E, int K, bool dsv3, int &tok_per_wg) {
+  const int mx = max_tok_per_wg(E, K, dsv3);
+  if (mx < 1) return 0;
   if (T <= kSingleMaxT && T <= mx) {
     tok_per_wg = T;
     return 1;
@@ -523,7 +531,7 @@ int launch_epl(const RouteArgs &a, hipStream_t s) {
   RouteParams P;
   P.a = a;
   const bool dsv3 = a.method == MOE_LORA_ROUTING_DEEPSEEK_V3;
-  const int nwg = plan_route(a.T, a.E, dsv3, P.tok_per_wg);
+  const int nwg = plan_route(a.T, a.E, a.K, dsv3, P.tok_per_wg);
   if (nwg <= 0) return ST_UNSUPPORTED;
   P.num_wg = nwg;
   const size_t lds = route_lds_bytes(a.E, a.K, P.tok_per_wg, dsv3);
@@ -541,14 +549,17 @@ int launch_epl(const RouteArgs &a, hipStream_t s) {
 
 }  // namespace
 
-size_t route_workspace_bytes(int T, int E) {
-  // enough for either routing method (DeepSeek-V3 uses the most workgroups)
-  int tpw = 0;
-  const int n = plan_route(T, E, true, tpw);
+size_t route_workspace_bytes(int T, int E, int K) {
+  // enough for either routing method
+  int tpw = 0, n = 0;
+  for (int m = 0; m < 2; ++m) {
+    const int nm = plan_route(T, E, K, m == 1, tpw);
+    n = nm > n ? nm : n;
+  }
   return n > 1 ? (size_t)n * E * sizeof(int32_t) : 0;
 }
 
-int route_max_tokens(int E) { return kMaxRouteWg * max_tok_per_wg(E); }
+int route_max_tokens(int E, int K, bool dsv3) { return kMaxRouteWg * max_tok_per_wg(E, K, dsv3); }
 
 int launch_zero_offsets(int32_t *offsets, int E, hipStream_t s) {
   zero_offsets_kernel<<<1, 256, 0, s>>>(offsets, E + 1);

@@ -249,37 +249,48 @@ class Workload:
 
     # -- stacked forms ---------------------------------------------------
     # -- FP8 expert weights (E4M3 codes + one fp32 scale per 128 x 128 block) --------
-    def _fp8_codes(self, shape, tensor: int, e: int) -> np.ndarray:
-        """Random E4M3 codes: uniform sign and mantissa, exponent field 4..7 (magnitudes
-        0.125 .. 1.875 before scaling); no NaN codes."""
+    # root mean square of the E4M3 values when every finite code is equally likely (the
+    # largest binade, 256 .. 448, dominates); scales divide it out for full-range codes
+    FP8_FULL_RANGE_RMS = 100.0
+
+    def _fp8_codes(self, shape, tensor: int, e: int, full_range: bool = False) -> np.ndarray:
+        """Random E4M3 codes.  Default: uniform sign and mantissa, exponent field 4..7
+        (magnitudes 0.125 .. 1.875 before scaling).  full_range: every finite code equally
+        likely (+-0, the subnormals, up to +-448); the two NaN codes 0x7f / 0xff never."""
         g = self._rng(tensor, 0, e)
+        if full_range:
+            c = g.integers(0, 254, size=shape, dtype=np.uint16)
+            return np.where(c >= 127, c + 1, c).astype(np.uint8)  # skip 0x7f
         sign = g.integers(0, 2, size=shape, dtype=np.uint8) << 7
         exp = g.integers(4, 8, size=shape, dtype=np.uint8) << 3
         man = g.integers(0, 8, size=shape, dtype=np.uint8)
         return sign | exp | man
 
-    def _fp8_scales(self, n: int, k: int, tensor: int, e: int, pow2: bool) -> np.ndarray:
+    def _fp8_scales(self, n: int, k: int, tensor: int, e: int, pow2: bool,
+                    full_range: bool = False) -> np.ndarray:
         """fp32 block scales around w_std: uniform in [0.5, 1.5) * w_std, or (pow2) the
-        power of two nearest w_std times 2^{-1, 0, 1}."""
+        power of two nearest w_std times 2^{-1, 0, 1}.  Full-range codes: around
+        w_std / FP8_FULL_RANGE_RMS instead."""
         c = self.cfg
+        std = c.w_std / self.FP8_FULL_RANGE_RMS if full_range else c.w_std
         shape = ((n + 127) // 128, (k + 127) // 128)
         g = self._rng(tensor, 0, e)
         if pow2:
-            base = np.round(np.log2(c.w_std))
+            base = np.round(np.log2(std))
             return np.ldexp(np.ones(shape, np.float32), (base + g.integers(-1, 2, size=shape)).astype(np.int32))
-        return (g.uniform(0.5, 1.5, size=shape) * c.w_std).astype(np.float32)
+        return (g.uniform(0.5, 1.5, size=shape) * std).astype(np.float32)
 
-    def w_gate_up_fp8(self, e: int, pow2: bool = False) -> tuple:
+    def w_gate_up_fp8(self, e: int, pow2: bool = False, full_range: bool = False) -> tuple:
         """Expert e's gate_up weight as (codes uint8 [2I, H], scales fp32 [2I/128, H/128])."""
         c = self.cfg
-        return (self._fp8_codes((2 * c.I, c.H), _T_W1_FP8, e),
-                self._fp8_scales(2 * c.I, c.H, _T_W1_SCALE, e, pow2))
+        return (self._fp8_codes((2 * c.I, c.H), _T_W1_FP8, e, full_range),
+                self._fp8_scales(2 * c.I, c.H, _T_W1_SCALE, e, pow2, full_range))
 
-    def w_down_fp8(self, e: int, pow2: bool = False) -> tuple:
+    def w_down_fp8(self, e: int, pow2: bool = False, full_range: bool = False) -> tuple:
         """Expert e's down weight as (codes uint8 [H, I], scales fp32 [H/128, I/128])."""
         c = self.cfg
-        return (self._fp8_codes((c.H, c.I), _T_W2_FP8, e),
-                self._fp8_scales(c.H, c.I, _T_W2_SCALE, e, pow2))
+        return (self._fp8_codes((c.H, c.I), _T_W2_FP8, e, full_range),
+                self._fp8_scales(c.H, c.I, _T_W2_SCALE, e, pow2, full_range))
 
     def _stack(self, fn, count: int, shape, experts: Optional[Sequence[int]] = None) -> np.ndarray:
         experts = list(range(count)) if experts is None else list(experts)

@@ -55,19 +55,23 @@ def assert_layer_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
     assert rel <= REL_L2_TOL and mx <= MAX_ABS_TOL, (what, rel, mx)
 
 
-def _stream_stack(wl: Workload, fn: str, shape, chunk: int = 8) -> torch.Tensor:
-    """Device tensor [E, *shape] filled expert-chunk by expert-chunk (bounded host memory)."""
+def _stream_stack(wl: Workload, fn: str, shape, chunk: int = 8, keep: Optional[dict] = None) -> torch.Tensor:
+    """Device tensor [E, *shape] filled expert-chunk by expert-chunk (bounded host memory
+    unless keep is given: then keep[e] holds expert e's host bits for the oracle)."""
     cfg = wl.cfg
     out = torch.empty((cfg.E,) + tuple(shape), dtype=torch.int16, device=dev())
     for e0, block in wl.expert_chunks(fn, chunk):
         out[e0:e0 + block.shape[0]].copy_(torch.from_numpy(block.view(np.int16)))
+        if keep is not None:
+            for i in range(block.shape[0]):
+                keep[e0 + i] = block[i]
     return out
 
 
 class GpuLayer:
     """A Workload's tensors on the GPU plus the oracle's view of the same bits."""
 
-    def __init__(self, wl: Workload, stream_weights: bool = False):
+    def __init__(self, wl: Workload, stream_weights: bool = False, keep_host: bool = False):
         self.wl = wl
         cfg = self.cfg = wl.cfg
         self.x_np, self.logits_np = wl.x(), wl.logits()
@@ -76,8 +80,11 @@ class GpuLayer:
         self.x, self.logits = t16(self.x_np), t16(self.logits_np)
         self.bias = torch.from_numpy(self.bias_np).to(dev()) if self.bias_np is not None else None
         if stream_weights:
-            self.w1 = _stream_stack(wl, "w_gate_up", (2 * cfg.I, cfg.H))
-            self.w2 = _stream_stack(wl, "w_down", (cfg.H, cfg.I))
+            # keep_host: the generated bits stay on the host for the oracle (22.5 GB at the
+            # DeepSeek-V3 share), instead of being regenerated per expert on demand
+            self._w1c, self._w2c = {}, {}
+            self.w1 = _stream_stack(wl, "w_gate_up", (2 * cfg.I, cfg.H), keep=self._w1c if keep_host else None)
+            self.w2 = _stream_stack(wl, "w_down", (cfg.H, cfg.I), keep=self._w2c if keep_host else None)
             self.w1_np = self.w2_np = None
         else:
             self.w1_np, self.w2_np = wl.w_gate_up_all(), wl.w_down_all()
@@ -94,16 +101,31 @@ class GpuLayer:
         return self.w2_np[e] if self.w2_np is not None else self._w2_cached(e)
 
     def _w1_cached(self, e):
-        c = self.__dict__.setdefault("_w1c", {})
+        c = self._w1c
         if e not in c:
             c[e] = self.wl.w_gate_up(e)
         return c[e]
 
     def _w2_cached(self, e):
-        c = self.__dict__.setdefault("_w2c", {})
+        c = self._w2c
         if e not in c:
             c[e] = self.wl.w_down(e)
         return c[e]
+
+    def packed_layer(self, mask: int) -> ml.MoELoRALayer:
+        """The same layer on tile-packed copies of the weights named by mask."""
+        c = self.cfg
+        return ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, self.w1, self.w2, self.routing, c.n_group,
+                               c.topk_group, c.routed_scaling_factor, self.bias, packed_weights=mask)
+
+    def oracle_layer(self, x_np=None, logits_np=None):
+        """Every token's output (and the routing) from the oracle, on the same bits."""
+        c = self.cfg
+        return oracle.layer(self.x_np if x_np is None else x_np,
+                            self.logits_np if logits_np is None else logits_np, c.top_k, c.I,
+                            self.w_gate_up, self.w_down, self.oracle_adapters(), self.slots_np, c.routing,
+                            self.bias_np, c.n_group, c.topk_group, c.routed_scaling_factor,
+                            num_experts=c.E)
 
     def oracle_adapters(self, shared_outer: bool = False):
         ads = []

@@ -4,6 +4,8 @@ Parity: the layer on E4M3 codes with 128 x 128 fp32 block scales against the fp6
 on the dequantized weights (tile heights 16, 64 and 128 with LoRA; decode without LoRA).
 Bit identity: with power-of-two block scales every dequantized weight is exact in bf16,
 so the FP8 kernels must give the same bits as the bf16 kernels run on those bf16 weights.
+Code range: one case draws every finite E4M3 code (+-0, the subnormals, up to +-448), so
+the hardware conversions (the general one and the fused scaled one) meet all of them.
 """
 
 import numpy as np
@@ -29,12 +31,12 @@ def _stack(fn, E):
 
 
 class Fp8Case:
-    def __init__(self, cfg, pow2=False):
+    def __init__(self, cfg, pow2=False, full_range=False):
         self.g = GpuLayer(Workload(cfg))
         c = self.cfg = cfg
         wl = self.g.wl
-        self.c1, self.s1 = _stack(lambda e: wl.w_gate_up_fp8(e, pow2), c.E)
-        self.c2, self.s2 = _stack(lambda e: wl.w_down_fp8(e, pow2), c.E)
+        self.c1, self.s1 = _stack(lambda e: wl.w_gate_up_fp8(e, pow2, full_range), c.E)
+        self.c2, self.s2 = _stack(lambda e: wl.w_down_fp8(e, pow2, full_range), c.E)
         self.dq1 = {}
         self.dq2 = {}
 
@@ -56,9 +58,10 @@ class Fp8Case:
                                w_gate_up_scale=t(self.s1), w_down_scale=t(self.s2),
                                fp8_pow2_scales=pow2_path)
 
-    def run(self, with_lora=True, packed=0, pow2_path=False):
+    def run(self, with_lora=True, packed=0, pow2_path=False, side=None):
         g = self.g
-        out = self.layer(packed, pow2_path)(g.x, g.logits, g.lora_slots() if with_lora else None)
+        out = self.layer(packed, pow2_path)(g.x, g.logits, g.lora_slots() if with_lora else None,
+                                            side_stream=side)
         torch.cuda.synchronize()
         return out.clone()
 
@@ -115,3 +118,49 @@ def test_fp8_packed_layouts_bit_identical(cfg):
     ref = case.run()
     for packed in (ml.PACKED_GATE_UP, ml.PACKED_DOWN, ml.PACKED_GATE_UP | ml.PACKED_DOWN):
         assert torch.equal(case.run(packed=packed), ref), packed
+
+
+FINITE_E4M3 = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], MID8], ids=["tiny", "mid-64row"])
+def test_fp8_every_finite_code(cfg):
+    """Weights whose codes span every finite E4M3 value: the general conversion (arbitrary
+    scales) within the bar of the oracle; with power-of-two scales both conversions within
+    the bar and bit-identical to the bf16 kernels on the exactly dequantized weights."""
+    say(f"[fp8 full code range] {cfg.name}")
+    case = Fp8Case(cfg, full_range=True)
+    for codes in (case.c1, case.c2):
+        np.testing.assert_array_equal(np.unique(codes), FINITE_E4M3)
+    assert_layer_close(f64(case.run()), case.oracle()["out"], f"fp8 all codes {cfg.name}")
+    case2 = Fp8Case(cfg, pow2=True, full_range=True)
+    ref = case2.oracle()["out"]
+    out8 = case2.run()
+    assert_layer_close(f64(out8), ref, f"fp8 all codes pow2 scales {cfg.name}")
+    assert torch.equal(case2.run(pow2_path=True, packed=ml.PACKED_GATE_UP | ml.PACKED_DOWN), out8)
+    c, g = case2.cfg, case2.g
+    layer16 = ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, _bf16_from_dequant(case2, 1),
+                              _bf16_from_dequant(case2, 2), g.routing, c.n_group, c.topk_group,
+                              c.routed_scaling_factor, g.bias)
+    out16 = layer16(g.x, g.logits, g.lora_slots())
+    torch.cuda.synchronize()
+    assert torch.equal(out8, out16)
+
+
+def test_fp8_with_side_stream_runs_the_fused_path():
+    """A side stream given to the FP8 entry point is left unused: the call runs the fused
+    path (the decomposed two-stream path is bf16 only) and gives the same bits."""
+    cfg = NAMED_CONFIGS[2]
+    say(f"[fp8 side stream] {cfg.name}")
+    case = Fp8Case(cfg)
+    ref = case.run()
+    side = torch.cuda.Stream()
+    out = case.run(side=side)
+    assert torch.equal(out, ref)
+    assert_layer_close(f64(out), case.oracle()["out"], "fp8 decode with a side stream")
+    opts = ml.Options()
+    opts.force_path = 2
+    g = case.g
+    with pytest.raises(ml.MoELoRAError) as ei:
+        case.layer()(g.x, g.logits, g.lora_slots(), side_stream=side, opts=opts)
+    assert ei.value.status == ml._lib.ERR_UNSUPPORTED

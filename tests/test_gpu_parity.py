@@ -125,13 +125,34 @@ def test_route_shapes_with_heavy_ties(T, E, k):
 
 
 @pytest.mark.parametrize("T,E,k,ng,tg", [(33, 16, 4, 4, 2), (257, 256, 8, 8, 4), (70, 64, 6, 64, 6),
-                                         (10, 32, 2, 1, 1)])
+                                         (10, 32, 2, 1, 1),
+                                         # E = 512: one workgroup holds at most 58 tokens (k = 8)
+                                         # or 53 (k = 32) beside the fp64 key rows
+                                         (58, 512, 8, 8, 4), (59, 512, 8, 8, 4), (64, 512, 8, 8, 4),
+                                         (53, 512, 32, 8, 4), (54, 512, 32, 8, 4),
+                                         (14848, 512, 8, 8, 4)])
 def test_route_deepseek_v3_shapes(T, E, k, ng, tg):
     say(f"[route dsv3] T={T} E={E} k={k} groups={ng}/{tg}")
     rng = np.random.default_rng(T + E)
     lg = rng.standard_normal((T, E)).astype(np.float32)
     bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
     _route_case(T, E, k, lg, "deepseek_v3", bias, ng, tg, 2.5)
+
+
+def test_route_token_limits_are_errors_not_faults():
+    """Batches past the documented per-call limit are refused before any launch."""
+    for T, E, k, dsv3 in [(14849, 512, 8, True), (16385, 512, 8, False), (65537, 128, 8, False)]:
+        d = ml.dims(T, 64, 64, E, k)
+        e = torch.empty((T * k,), dtype=torch.int32, device=dev())
+        off = torch.empty((E + 1,), dtype=torch.int32, device=dev())
+        lg = torch.zeros((T, E), dtype=torch.int16, device=dev())
+        ws = torch.zeros((max(1, ml.moe_lora_route_workspace_size(d)),), dtype=torch.uint8, device=dev())
+        grouped = ml.Grouped(8, 4, 1.0, None) if dsv3 else None
+        r = ml.ROUTING_DEEPSEEK_V3 if dsv3 else ml.ROUTING_RENORMALIZE
+        with pytest.raises(ml.MoELoRAError) as ei:
+            ml.moe_lora_route(d, lg, e, torch.empty((T * k,), device=dev()), off, e, e, ws, r, grouped)
+        assert ei.value.status == ml._lib.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
 
 
 def test_route_deepseek_v3_exact_ties():
@@ -233,21 +254,69 @@ def test_gather_on_load_equals_permuted_input_and_is_deterministic():
     assert torch.equal(a, c)
 
 
-def test_layer_parity_prefill_sampled():
+def _route_of(layer, T, lora):
+    rt = layer.last_route(T, lora)
+    return {"ids": rt.topk_ids.cpu().numpy(), "w": rt.topk_weights.cpu().numpy(),
+            "off": rt.expert_offsets.cpu().numpy(), "e2p": rt.e2p.cpu().numpy(),
+            "p2e": rt.p2e.cpu().numpy()}
+
+
+def _tiles(offsets, bm, ncols):
+    """(m-tile, n-tile) work tiles of one GEMM launch for the realized expert offsets."""
+    counts = np.diff(np.asarray(offsets, dtype=np.int64))
+    return int(((counts + bm - 1) // bm).sum()) * ncols
+
+
+def test_layer_parity_prefill_every_token():
+    """Prefill at full size (8192 tokens, skewed loads, 128 x 256 persistent tiles): routing
+    bit-exact and every token's output within the bar, on row-major weights and on the
+    tile-packed weights the benchmark times (the two bit-identical)."""
     cfg = NAMED_CONFIGS[3]
     g = gpu_layer(cfg)
-    say(f"[layer] {cfg.name}: routing on all tokens, output on sampled tokens")
+    say(f"[layer] {cfg.name}: every token, row-major and tile-packed weights")
     layer, lora, out = _layer_case(g)
-    rt = layer.last_route(cfg.T, lora)
-    ids, w = g.oracle_route()
-    check_route({"ids": rt.topk_ids.cpu().numpy(), "w": rt.topk_weights.cpu().numpy(),
-                 "off": rt.expert_offsets.cpu().numpy(), "e2p": rt.e2p.cpu().numpy(),
-                 "p2e": rt.p2e.cpu().numpy()}, ids, w, cfg.E)
-    rng = np.random.default_rng(0)
-    toks = np.sort(np.concatenate([rng.choice(cfg.T, 200, replace=False), [0, cfg.T - 1]]))
-    ref = oracle.layer_sampled(g.x_np, ids, w, toks, cfg.I, g.w_gate_up, g.w_down, g.oracle_adapters(),
-                               g.slots_np)
-    assert_layer_close(f64(out)[toks], ref, "prefill sampled")
+    packed = g.packed_layer(ml.PACKED_GATE_UP | ml.PACKED_DOWN)
+    out_p = packed(g.x, g.logits, lora).clone()
+    torch.cuda.synchronize()
+    ref = g.oracle_layer()
+    check_route(_route_of(layer, cfg.T, lora), ref["ids"], ref["weights"], cfg.E)
+    assert_layer_close(f64(out), ref["out"], "prefill row-major, every token")
+    assert torch.equal(out, out_p), "tile-packed weights changed the prefill output"
+
+
+@pytest.mark.timeout(900)
+def test_layer_parity_dsv3_full_weights_every_token():
+    """DeepSeek-V3-style layer at full size (256 experts resident, ~22.5 GB of bf16
+    weights, 64-row persistent tiles): routing bit-exact and every token's output within the
+    bar on row-major weights; the tile-packed weights the benchmark times give the same bits.
+    With at least eight 64-row tiles per resident block (at most 512 blocks: two 4-wave
+    blocks per CU at two waves per SIMD) both packed GEMMs walk the tiles in launch order,
+    which is checked to be the case here."""
+    cfg = NAMED_CONFIGS[5]
+    _CACHE.clear()
+    torch.cuda.empty_cache()
+    say(f"[layer] {cfg.name}: full weights resident, every token")
+    g = GpuLayer(Workload(cfg, 0), stream_weights=True, keep_host=True)
+    layer, lora, out = _layer_case(g)
+    rt = _route_of(layer, cfg.T, lora)
+    # 64-row tiles here; gate_up tiles cover 64 intermediate columns, down tiles 128 outputs
+    assert 8 < cfg.R // cfg.E <= 128
+    resident_max = 2 * 256
+    assert _tiles(rt["off"], 64, cfg.I // 64) >= 8 * resident_max
+    assert _tiles(rt["off"], 64, cfg.H // 128) >= 8 * resident_max
+    say("  packing the weights")
+    packed = g.packed_layer(ml.PACKED_GATE_UP | ml.PACKED_DOWN)
+    out_p = packed(g.x, g.logits, lora).clone()
+    torch.cuda.synchronize()
+    del packed
+    torch.cuda.empty_cache()
+    assert torch.equal(out, out_p), "tile-packed weights changed the output"
+    say("  oracle on every token")
+    ref = g.oracle_layer()
+    check_route(rt, ref["ids"], ref["weights"], cfg.E)
+    assert_layer_close(f64(out), ref["out"], "dsv3 every token")
+    del g
+    torch.cuda.empty_cache()
 
 
 def test_empty_batch():
@@ -260,33 +329,6 @@ def test_empty_batch():
     ml.moe_lora_route(d, g.logits[:0], e, torch.empty((0,), device=dev()), off, e, e, None)
     torch.cuda.synchronize()
     assert (off.cpu() == 0).all()
-
-
-@pytest.mark.timeout(900)
-def test_layer_parity_dsv3_full_weights_sampled():
-    """DeepSeek-V3-style layer at full size (256 experts resident, ~22.5 GB of bf16
-    weights): routing bit-exact on all tokens, outputs on sampled tokens."""
-    from concurrent.futures import ThreadPoolExecutor
-
-    cfg = NAMED_CONFIGS[5]
-    g = gpu_layer(cfg, stream_weights=True)
-    say(f"[layer] {cfg.name}: full weights resident")
-    layer, lora, out = _layer_case(g)
-    rt = layer.last_route(cfg.T, lora)
-    ids, w = g.oracle_route()
-    check_route({"ids": rt.topk_ids.cpu().numpy(), "w": rt.topk_weights.cpu().numpy(),
-                 "off": rt.expert_offsets.cpu().numpy(), "e2p": rt.e2p.cpu().numpy(),
-                 "p2e": rt.p2e.cpu().numpy()}, ids, w, cfg.E)
-    toks = np.array([0, 1, 333, 777, 1000, cfg.T - 1])
-    experts = sorted(set(int(e) for e in ids[toks].reshape(-1)))
-    say(f"  generating {len(experts)} experts' weights for the oracle")
-    with ThreadPoolExecutor(16) as ex:
-        list(ex.map(lambda e: (g.w_gate_up(e), g.w_down(e)), experts))
-    ref = oracle.layer_sampled(g.x_np, ids, w, toks, cfg.I, g.w_gate_up, g.w_down, g.oracle_adapters(),
-                               g.slots_np)
-    assert_layer_close(f64(out)[toks], ref, "dsv3 sampled")
-    _CACHE.clear()
-    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("cfg", [NAMED_CONFIGS[2], NAMED_CONFIGS[4], RAGGED], ids=lambda c: c.name)
