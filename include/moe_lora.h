@@ -20,7 +20,9 @@
  *   - The caller owns every buffer, including the workspaces sized by the
  *     *_workspace_size functions; the library never allocates device memory
  *     (the capture-safety lesson of sglang PR "[LoRA] Fix experimental fast-path
- *     multi-adapter correctness ...", Motivation item 3 and Modifications).
+ *     multi-adapter correctness ...", Motivation item 3 and Modifications).  The one
+ *     exception is static: the fixed scratch array of moe_lora_forward_noalloc, part
+ *     of the library's code object on each GPU.
  *   - Work is enqueued on the given stream(s) (a hipStream_t passed as void*;
  *     NULL = the null stream) and is asynchronous.  No call synchronizes the device.
  *   - Errors: arguments are validated on the host first; on any error nothing is
@@ -48,7 +50,8 @@ typedef enum {
   MOE_LORA_ERR_INVALID_ARGUMENT = 1,
   MOE_LORA_ERR_UNSUPPORTED = 2,
   MOE_LORA_ERR_WORKSPACE_TOO_SMALL = 3,
-  MOE_LORA_ERR_HIP = 4
+  MOE_LORA_ERR_HIP = 4,
+  MOE_LORA_ERR_SCRATCH_TOO_SMALL = 5 /* moe_lora_forward_noalloc: the problem needs more scratch */
 } moe_lora_status;
 
 /* Routing methods (vLLM API page "trtllm_lora_moe", TrtLlmBf16LoRAExperts
@@ -63,6 +66,8 @@ typedef enum {
 #define MOE_LORA_MAX_RANK 64   /* direct-expand limit, section 2 of the bf16 PR */
 #define MOE_LORA_MAX_EXPERTS 512
 #define MOE_LORA_MAX_TOPK 32
+/* fixed per-GPU scratch of moe_lora_forward_noalloc (64 MiB) */
+#define MOE_LORA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Problem size (the (E, M, N=2I, K=H, topk) tuple of the vLLM API page,
  * _TrtLlmLoRAExpertsBase.moe_problem_size). */
@@ -207,6 +212,33 @@ int moe_lora_forward(const moe_lora_dims *dims, const uint16_t *x, const uint16_
                      const moe_lora_adapters *lora, uint16_t *y_perm, void *ws, size_t ws_bytes,
                      moe_lora_stream_t main, moe_lora_stream_t side,
                      const moe_lora_options *opts);
+
+/* ---------------------------------------------------------------- forward, no allocation
+ * For callers that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  moe_lora_forward on one
+ * stream (the fused path) with its workspace taken from a scratch array the library holds
+ * on each GPU it runs on: MOE_LORA_NOALLOC_SCRATCH_BYTES of device memory, reserved when
+ * the library's code is loaded on that GPU and kept until the process ends.  The call
+ * makes no allocation of any kind.
+ *   Arguments as for moe_lora_forward (x or x_perm, routing outputs, weights, lora,
+ *   y_perm: caller-owned device buffers).  opts: as for moe_lora_forward, except that
+ *   force_path = 2 (the decomposed path) -> MOE_LORA_ERR_UNSUPPORTED; there is no side
+ *   stream.
+ *   Returns MOE_LORA_ERR_SCRATCH_TOO_SMALL, enqueuing nothing, when the problem's fused
+ *   workspace (moe_lora_forward_workspace_size without the decomposed path's buffers)
+ *   exceeds the scratch: the decode-sized batches fit (64 tokens of a hidden-2048,
+ *   128-expert, top-8 layer with a rank-16 adapter need ~1.4 MiB; 256 tokens with four
+ *   adapters up to rank 64 ~10 MiB); 8192-token prefill batches of that layer (154 MiB)
+ *   and 1024 tokens of a hidden-7168, 256-expert layer (68 MiB) do not.
+ * Concurrency: every call on one GPU uses the same scratch, which keeps the last call's
+ * contents (nothing in it needs to start at zero).  Calls that overlap on one GPU, from
+ * several host threads or on several streams without ordering between them, race on it
+ * and give wrong results; order them on one stream. */
+int moe_lora_forward_noalloc(const moe_lora_dims *dims, const uint16_t *x, const uint16_t *x_perm,
+                             const int32_t *expert_offsets, const int32_t *permuted_to_expanded,
+                             const uint16_t *w_gate_up, const uint16_t *w_down,
+                             const moe_lora_adapters *lora, uint16_t *y_perm, moe_lora_stream_t main,
+                             const moe_lora_options *opts);
 
 /* ---------------------------------------------------------------- forward, FP8 weights
  * moe_lora_forward with FP8 expert weights (fast-path PR, title and Optimizations: the

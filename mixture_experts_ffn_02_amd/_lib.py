@@ -20,6 +20,8 @@ ERR_INVALID_ARGUMENT = 1
 ERR_UNSUPPORTED = 2
 ERR_WORKSPACE_TOO_SMALL = 3
 ERR_HIP = 4
+ERR_SCRATCH_TOO_SMALL = 5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 ROUTING_RENORMALIZE = 0
 ROUTING_DEEPSEEK_V3 = 1
@@ -36,6 +38,7 @@ EXPORTED = (
     "moe_lora_permute",
     "moe_lora_forward_workspace_size",
     "moe_lora_forward",
+    "moe_lora_forward_noalloc",
     "moe_lora_forward_fp8",
     "moe_lora_pack_weights",
     "moe_lora_pack_weights_fp8",
@@ -108,6 +111,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_lora_forward.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, POINTER(Adapters), c_void_p, c_void_p,
                                      c_size_t, c_void_p, c_void_p, POINTER(Options)]
+    lib.moe_lora_forward_noalloc.restype = c_int
+    lib.moe_lora_forward_noalloc.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, POINTER(Adapters), c_void_p, c_void_p,
+                                             POINTER(Options)]
     lib.moe_lora_forward_fp8.restype = c_int
     lib.moe_lora_forward_fp8.argtypes = [POINTER(Dims), c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, POINTER(Adapters),

@@ -2,8 +2,16 @@
 // The contract of every call is documented in include/moe_lora.h.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
+
+// Scratch of moe_lora_forward_noalloc: one fixed device array per GPU, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel or a copy (on the host
+// the name is only a stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current (scratch_address).
+static __device__ __attribute__((aligned(256))) unsigned char scratch[MOE_LORA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -49,6 +57,24 @@ int check_lora(const moe_lora_adapters *l) {
   return MOE_LORA_OK;
 }
 
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// device address of the current device's scratch array (looked up on the first call there)
+int scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_LORA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_LORA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_LORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -60,6 +86,8 @@ const char *moe_lora_status_string(int status) {
     case MOE_LORA_ERR_UNSUPPORTED: return "unsupported shape or parameter";
     case MOE_LORA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MOE_LORA_ERR_HIP: return "HIP launch error";
+    case MOE_LORA_ERR_SCRATCH_TOO_SMALL:
+      return "problem needs more than the fixed scratch of moe_lora_forward_noalloc (64 MiB)";
     default: return "unknown status";
   }
 }
@@ -186,7 +214,7 @@ int forward_checked(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x
                     const void *w_down, const float *w1_scale, const float *w2_scale,
                     const moe_lora_adapters *lora, uint16_t *y_perm, void *ws, size_t ws_bytes,
                     moe_lora_stream_t main, moe_lora_stream_t side, const moe_lora_options *opts,
-                    bool fp8) {
+                    bool fp8, bool noalloc = false) {
   int st = check_dims(d);
   if (st != MOE_LORA_OK) return st;
   if ((st = check_lora(lora)) != MOE_LORA_OK) return st;
@@ -195,6 +223,7 @@ int forward_checked(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x
   if (opts && (opts->fp8_pow2_scales < 0 || opts->fp8_pow2_scales > 1)) return MOE_LORA_ERR_INVALID_ARGUMENT;
   if (opts && opts->packed_weights && (d->hidden % 128 != 0 || d->inter % 64 != 0))
     return MOE_LORA_ERR_UNSUPPORTED;
+  if (noalloc && opts && opts->force_path == 2) return MOE_LORA_ERR_UNSUPPORTED;
   if (fp8) {
     if (d->hidden % 128 != 0 || d->inter % 128 != 0) return MOE_LORA_ERR_UNSUPPORTED;
     if (d->hidden > 8192 || d->inter > 8192) return MOE_LORA_ERR_UNSUPPORTED;  // per-tile scale table
@@ -210,13 +239,19 @@ int forward_checked(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x
     return MOE_LORA_ERR_INVALID_ARGUMENT;
   if (fp8 && (!w1_scale || !w2_scale || !aligned16(w1_scale) || !aligned16(w2_scale)))
     return MOE_LORA_ERR_INVALID_ARGUMENT;
-  const size_t need = moe::forward_workspace_size(*d, lora);
+  const size_t need = moe::forward_workspace_size(*d, lora, noalloc);
+  if (noalloc) {
+    if (need > (size_t)MOE_LORA_NOALLOC_SCRATCH_BYTES) return MOE_LORA_ERR_SCRATCH_TOO_SMALL;
+    if ((st = scratch_address(&ws)) != MOE_LORA_OK) return st;
+    ws_bytes = MOE_LORA_NOALLOC_SCRATCH_BYTES;
+    side = nullptr;
+  }
   if (ws_bytes < need) return MOE_LORA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && (!ws || !aligned16(ws))) return MOE_LORA_ERR_INVALID_ARGUMENT;
   return moe::launch_forward(*d, x, x_perm, expert_offsets, p2e, static_cast<const uint16_t *>(w_gate_up),
                              static_cast<const uint16_t *>(w_down), lora, y_perm, ws, ws_bytes,
                              reinterpret_cast<hipStream_t>(main), reinterpret_cast<hipStream_t>(side), opts,
-                             fp8 ? w1_scale : nullptr, fp8 ? w2_scale : nullptr);
+                             fp8 ? w1_scale : nullptr, fp8 ? w2_scale : nullptr, noalloc);
 }
 
 }  // namespace
@@ -228,6 +263,14 @@ int moe_lora_forward(const moe_lora_dims *d, const uint16_t *x, const uint16_t *
                      const moe_lora_options *opts) {
   return forward_checked(d, x, x_perm, expert_offsets, p2e, w_gate_up, w_down, nullptr, nullptr, lora,
                          y_perm, ws, ws_bytes, main, side, opts, false);
+}
+
+int moe_lora_forward_noalloc(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x_perm,
+                             const int32_t *expert_offsets, const int32_t *p2e, const uint16_t *w_gate_up,
+                             const uint16_t *w_down, const moe_lora_adapters *lora, uint16_t *y_perm,
+                             moe_lora_stream_t main, const moe_lora_options *opts) {
+  return forward_checked(d, x, x_perm, expert_offsets, p2e, w_gate_up, w_down, nullptr, nullptr, lora,
+                         y_perm, nullptr, 0, main, nullptr, opts, false, true);
 }
 
 int moe_lora_forward_fp8(const moe_lora_dims *d, const uint16_t *x, const uint16_t *x_perm,

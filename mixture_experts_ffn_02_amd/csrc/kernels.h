@@ -42,12 +42,13 @@ int launch_pack_weights(const moe_lora_dims &d, const uint16_t *w1, const uint16
                         uint16_t *w2p, hipStream_t s);
 
 // ---- expert FFN (grouped GEMMs + LoRA) -----------------------------------------
-size_t forward_workspace_size(const moe_lora_dims &d, const moe_lora_adapters *lora);
+// fused_only: the workspace (and the call) leave out the decomposed two-stream path
+size_t forward_workspace_size(const moe_lora_dims &d, const moe_lora_adapters *lora, bool fused_only = false);
 int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_perm,
                    const int32_t *offsets, const int32_t *p2e, const uint16_t *w1,
                    const uint16_t *w2, const moe_lora_adapters *lora, uint16_t *y_perm, void *ws,
                    size_t ws_bytes, hipStream_t main, hipStream_t side,
                    const moe_lora_options *opts, const float *w1_scale = nullptr,
-                   const float *w2_scale = nullptr);
+                   const float *w2_scale = nullptr, bool fused_only = false);
 
 }  // namespace moe

@@ -1368,7 +1368,8 @@ struct FwdLayout {
 constexpr int kReduceMinSplits = 4;
 constexpr long long kReduceMinBytes = 32ll << 20;
 
-FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
+// fused_only: no room for the decomposed path's fp32 G / delta buffers
+FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora, bool fused_only = false) {
   FwdLayout L;
   const size_t R = (size_t)d.num_tokens * d.top_k;
   const bool has_lora = lora && lora->num_slots > 0;
@@ -1392,7 +1393,7 @@ FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
     L.v_red = off;
     off = align256(off + R * L.rmax * sizeof(uint16_t));
   }
-  if (has_lora && d.num_tokens <= kTwoStreamMaxT && (d.inter % 4) == 0) {
+  if (!fused_only && has_lora && d.num_tokens <= kTwoStreamMaxT && (d.inter % 4) == 0) {
     L.decomposed = true;
     L.g = off;
     off = align256(off + R * 2 * d.inter * sizeof(float));
@@ -1405,21 +1406,22 @@ FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora) {
 
 }  // namespace
 
-size_t forward_workspace_size(const moe_lora_dims &d, const moe_lora_adapters *lora) {
-  return layout(d, lora).total;
+size_t forward_workspace_size(const moe_lora_dims &d, const moe_lora_adapters *lora, bool fused_only) {
+  return layout(d, lora, fused_only).total;
 }
 
 int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_perm,
                    const int32_t *offsets, const int32_t *p2e, const uint16_t *w1,
                    const uint16_t *w2, const moe_lora_adapters *lora, uint16_t *y_perm, void *ws,
                    size_t ws_bytes, hipStream_t main, hipStream_t side,
-                   const moe_lora_options *opts, const float *w1_scale, const float *w2_scale) {
+                   const moe_lora_options *opts, const float *w1_scale, const float *w2_scale,
+                   bool fused_only) {
   const int R = d.num_tokens * d.top_k;
   // FP8 weights (w1/w2 hold E4M3 codes, block scales given): fused path only
   const bool fp8 = w1_scale != nullptr;
   const bool pow2 = fp8 && opts && opts->fp8_pow2_scales;  // power-of-two block scales
   if (R == 0) return ST_OK;
-  const FwdLayout L = layout(d, lora);
+  const FwdLayout L = layout(d, lora, fused_only);
   if (ws_bytes < L.total) return ST_WS_SMALL;
   char *wsb = static_cast<char *>(ws);
   const bool has_lora = lora && lora->num_slots > 0;

@@ -113,6 +113,15 @@ def moe_lora_forward(d: Dims, x, x_perm, expert_offsets, p2e, w_gate_up, w_down,
         ctypes.byref(opts) if opts is not None else None))
 
 
+def moe_lora_forward_noalloc(d: Dims, x, x_perm, expert_offsets, p2e, w_gate_up, w_down,
+                             lora: Optional[Adapters], y_perm, main=None,
+                             opts: Optional[Options] = None) -> None:
+    check("moe_lora_forward_noalloc", load().moe_lora_forward_noalloc(
+        ctypes.byref(d), _ptr(x), _ptr(x_perm), _ptr(expert_offsets), _ptr(p2e), _ptr(w_gate_up),
+        _ptr(w_down), ctypes.byref(lora) if lora is not None else None, _ptr(y_perm), _stream(main),
+        ctypes.byref(opts) if opts is not None else None))
+
+
 def moe_lora_forward_fp8(d: Dims, x, x_perm, expert_offsets, p2e, w_gate_up, w_gate_up_scale, w_down,
                          w_down_scale, lora: Optional[Adapters], y_perm, ws, main=None, side=None,
                          opts: Optional[Options] = None) -> None:
