@@ -1464,6 +1464,12 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   if (force == 2 && has_lora && !L.decomposed) return ST_UNSUPPORTED;
   // the side stream is used only by the decomposed path
   hipStream_t lora_stream = (decomposed && side) ? side : main;
+  // The down-LoRA shrink v = A2 . act: contracted in the gate_up epilogue (partials per
+  // n-tile) for 16- and 128-row tiles, a separate split-K shrink launch over act for 64-row
+  // tiles, whose epilogue contraction cost more than the launch (multi-adapter T=256: step
+  // 319 -> 312 us, gate_up 166 -> 145 us; DeepSeek-V3-sized: 3.23 -> 3.18 ms; decode T=64
+  // +2 us and prefill even with the launch), and always on the decomposed path.
+  const bool sep_down_shrink = decomposed || (has_lora && bm == 64);
 
   GemmParams shrink1 = base;
   if (has_lora) {  // gate_up LoRA shrink: u_part = A1 . x  (split over H)
@@ -1497,7 +1503,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       gu.row_slot = row_slot;
     }
     gu.out_bf16 = act;
-    if (has_lora) {  // the down-LoRA shrink rides in the epilogue (partials per I tile)
+    if (has_lora && !sep_down_shrink) {  // the down-LoRA shrink rides in the epilogue (partials per I tile)
       for (int s = 0; s < lora->num_slots; ++s) gu.down_a[s] = lora->a_down[s];
       gu.down_part = v_part;
     }
@@ -1543,7 +1549,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   }
   // 3) down LoRA shrink: v_part = A2 . act  (split over I); fused into the gate_up
   //    epilogue on the fused path
-  if (has_lora && decomposed) {
+  if (has_lora && sep_down_shrink) {
     GemmParams P = base;
     P.a = act;
     P.a_gather = 0;
@@ -1570,7 +1576,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->b_down[s];
       P.lora_w_shared = lora->shared_outer;  // shared-outer: one B2 for all experts
       P.part = v_part;
-      P.part_splits = decomposed ? L.shrink2_splits : gateup_ncols(bm, d.inter);
+      P.part_splits = sep_down_shrink ? L.shrink2_splits : gateup_ncols(bm, d.inter);
       P.row_slot = row_slot;
       const long long down_ntiles = cdiv(d.hidden, bm >= 128 ? 256 : 128);
       const long long reread = down_ntiles * P.part_splits * R * L.rmax * (long long)sizeof(float);
