@@ -102,6 +102,9 @@ struct GemmParams {
   // the later LoRA kernels instead of token_slot[p2e[p] / k] (one dependent load fewer)
   int32_t *row_slot_out;
   const int32_t *row_slot;
+  // persistent tiles only: walk each expert's tiles m-tile first (the m-tiles that read one
+  // weight slice run side by side on one XCD and share it in its L2) in per-XCD shares
+  int mt_fast;
 };
 
 // Register budget: two waves per SIMD (256 VGPRs) for every tile height.  Three waves on
@@ -222,7 +225,7 @@ void moe_gemm_kernel(const GemmParams P) {
     L = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
     L_end = min(total, (int)(blockIdx.x & 7) * per_xcd + per_xcd);
     L_step = (int)(gridDim.x >> 3);
-    if (BM <= 64 && P.w_packed && total >= 8 * (int)gridDim.x) {
+    if (BM <= 64 && P.w_packed && !P.mt_fast && total >= 8 * (int)gridDim.x) {
       // 64-row tiles, many per block: on packed weights the grid walks the tiles in
       // launch order, front to back through the packed buffer (DeepSeek-V3-sized layer,
       // 16 and 28 tiles per block: 3.53 -> 3.28 ms).  128-row tiles keep the per-XCD
@@ -243,7 +246,9 @@ void moe_gemm_kernel(const GemmParams P) {
   }
   int parity = 0;
   for (; L < L_end; L += L_step, parity ^= 1) {
-  const int mt = L / P.n_cols, col = L % P.n_cols;
+  // tile L -> (m-tile, column): column fastest, or m-tile fastest within the expert (the
+  // expert's tiles fill the same range of L either way)
+  int mt = L / P.n_cols, col = L % P.n_cols;
   // expert of m-tile mt: last e with s_tpre[e] <= mt (binary search, same in every lane)
   int lo_e = 0, hi_e = P.E;  // invariant: s_tpre[lo_e] <= mt < s_tpre[hi_e]
   while (hi_e - lo_e > 1) {
@@ -252,6 +257,13 @@ void moe_gemm_kernel(const GemmParams P) {
     else hi_e = mid;
   }
   const int e = __builtin_amdgcn_readfirstlane(lo_e);  // block-uniform values in SGPRs
+  if (kPersistent && P.mt_fast) {
+    const int t0 = __builtin_amdgcn_readfirstlane(s_tpre[e]);
+    const int nm = __builtin_amdgcn_readfirstlane(s_tpre[e + 1]) - t0;
+    const int local = L - t0 * P.n_cols;
+    col = local / nm;
+    mt = t0 + local % nm;
+  }
   const int cnt = __builtin_amdgcn_readfirstlane(s_off[e + 1] - s_off[e]);
   const int m0 = (mt - __builtin_amdgcn_readfirstlane(s_tpre[e])) * BM;
   const int row0 = __builtin_amdgcn_readfirstlane(s_off[e]) + m0;
@@ -1491,6 +1503,12 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   gu.N = 2 * d.inter;
   gu.w_packed = packed & 1;
   gu.w_scale = w1_scale;
+  // Tile order, per GEMM and tile height, as measured (HBM reads from FETCH_SIZE): m-tile
+  // first on the 64-row gate_up tiles (DeepSeek-V3-sized: 13.9 -> 12.3 GB read, 1.92 ->
+  // 1.86 ms; multi-adapter even) and the 128-row down tiles (prefill: 0.91 -> 0.73 GB,
+  // 380 -> 363 us); column first elsewhere (the 64-row down tiles read 0.9 GB less but took
+  // 1.10 -> 1.15 ms; 128-row gate_up 568 -> 575 us)
+  gu.mt_fast = (bm == 64);
 
   if (!decomposed) {
     // fused: shrink, then the GEMM appends the LoRA expand as extra K steps and applies
@@ -1572,6 +1590,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     P.N = d.hidden;
     P.w_packed = (packed >> 1) & 1;
     P.w_scale = w2_scale;
+    P.mt_fast = (bm >= 128);  // (see the gate_up GEMM)
     if (has_lora) {
       for (int s = 0; s < lora->num_slots; ++s) P.lora_w[s] = lora->b_down[s];
       P.lora_w_shared = lora->shared_outer;  // shared-outer: one B2 for all experts
