@@ -176,8 +176,10 @@ class Workbench:
         return o
 
     def back_to_back(self, layer, lora, steps, warmup, gate_up=False, side=None, opts=None):
-        """K steps back to back between two device synchronizations (wall clock), and the
-        mean gate_up GEMM time from the library-recorded events."""
+        """K steps back to back between two device synchronizations (wall clock); with
+        gate_up, also the mean gate_up GEMM time from events the library records around its
+        launch (those events idle the GPU between kernels, so such steps are not timed for
+        the step time)."""
         import torch
 
         evs = Events(2 * steps) if gate_up else None
@@ -193,10 +195,13 @@ class Workbench:
         gu = sum(evs.ms(2 * i, 2 * i + 1) for i in range(steps)) / steps if gate_up else None
         return dt, gu
 
-    def flushed(self, layer, lora, reps, warmup, flush, side=None):
+    def flushed(self, layer, lora, reps, warmup, flush, side=None, gate_up=False):
         """Per-step HIP-event times with a 1 GiB scratch read before every step (outside the
         events: it evicts L2 and the 256 MB MALL without leaving dirty lines whose write-back
-        would fall inside the step); returns the step and gate_up times in ms, one per rep."""
+        would fall inside the step); returns the step times in ms, one per rep, or with
+        gate_up the gate_up GEMM's times from events the library records around its launch.
+        An event recorded between two kernels idles the GPU for ~6 us, so the step times
+        come from reps without the gate_up events and the kernel times from reps of their own."""
         import numpy as np
         import torch
 
@@ -204,16 +209,16 @@ class Workbench:
             flush.sum()
             self.step(layer, lora, side=side)
         steps = Events(2 * reps)
-        gus = Events(2 * reps)
+        gus = Events(2 * reps) if gate_up else None
         for i in range(reps):
             flush.sum()
             steps.ev[2 * i].record()
-            self.step(layer, lora, self.gate_up_opts(gus, i), side)
+            self.step(layer, lora, self.gate_up_opts(gus, i) if gate_up else None, side)
             steps.ev[2 * i + 1].record()
         torch.cuda.synchronize()
-        st = np.array([steps.ms(2 * i, 2 * i + 1) for i in range(reps)])
-        gu = np.array([gus.ms(2 * i, 2 * i + 1) for i in range(reps)])
-        return st, gu
+        if gate_up:
+            return np.array([gus.ms(2 * i, 2 * i + 1) for i in range(reps)])
+        return np.array([steps.ms(2 * i, 2 * i + 1) for i in range(reps)])
 
     def counts(self):
         """Algorithmic bytes and flops of one step from the realized routing (weights of
@@ -329,8 +334,10 @@ def measure_flushed(wb: Workbench, reps: int, warmup: int, flush, log) -> dict:
     """The flushed protocol on one workload: LoRA on and off (same kernels, no adapters)."""
     cfg = wb.cfg
     log(f"flushed protocol: {cfg.name}, {reps} reps")
-    st_on, gu_on = wb.flushed(wb.layer, wb.lora, reps, warmup, flush)
-    st_off, gu_off = wb.flushed(wb.layer, None, reps, warmup, flush)
+    st_on = wb.flushed(wb.layer, wb.lora, reps, warmup, flush)
+    st_off = wb.flushed(wb.layer, None, reps, warmup, flush)
+    gu_on = wb.flushed(wb.layer, wb.lora, reps, warmup, flush, gate_up=True)
+    gu_off = wb.flushed(wb.layer, None, reps, warmup, flush, gate_up=True)
     import numpy as np
 
     c = wb.counts()
@@ -356,7 +363,7 @@ def measure_flushed(wb: Workbench, reps: int, warmup: int, flush, log) -> dict:
         import torch
 
         side = torch.cuda.Stream()
-        st_two, _ = wb.flushed(wb.layer, wb.lora, reps, warmup, flush, side=side)
+        st_two = wb.flushed(wb.layer, wb.lora, reps, warmup, flush, side=side)
         out["two_stream_step_ms"] = {"median": round(float(np.median(st_two)), 4), "p10": pct(st_two, 10),
                                      "p90": pct(st_two, 90)}
     if cfg.T <= 16:
@@ -369,11 +376,10 @@ def run_only(wb: Workbench, leg: str, steps: int, warmup: int):
     import torch
 
     res = {"workload": wb.cfg.name, "leg": leg}
-    if leg == "lora-on":
-        t, gu = wb.back_to_back(wb.layer, wb.lora, steps, warmup, gate_up=True)
-        res["gate_up_us"] = round(gu * 1e3, 2)
-    elif leg == "lora-off":
-        t, gu = wb.back_to_back(wb.layer, None, steps, warmup, gate_up=True)
+    if leg in ("lora-on", "lora-off"):
+        lr = wb.lora if leg == "lora-on" else None
+        t, _ = wb.back_to_back(wb.layer, lr, steps, warmup)
+        _, gu = wb.back_to_back(wb.layer, lr, max(2, steps // 4), 1, gate_up=True)
         res["gate_up_us"] = round(gu * 1e3, 2)
     elif leg == "two-stream":
         side = torch.cuda.Stream()
@@ -394,7 +400,9 @@ def run_only(wb: Workbench, leg: str, steps: int, warmup: int):
         t = graph_replay(wb, steps, warmup)
     else:
         l8, l8p = wb.fp8_layers()
-        t, gu = wb.back_to_back(l8 if leg == "fp8" else l8p, wb.lora, steps, warmup, gate_up=True)
+        lyr = l8 if leg == "fp8" else l8p
+        t, _ = wb.back_to_back(lyr, wb.lora, steps, warmup)
+        _, gu = wb.back_to_back(lyr, wb.lora, max(2, steps // 4), 1, gate_up=True)
         res["gate_up_us"] = round(gu * 1e3, 2)
     res["ms_per_step"] = round(t * 1e3, 4)
     return res
@@ -444,9 +452,12 @@ def main():
 
     # ---- headline: K back-to-back steps between two synchronizations
     log("timing LoRA on (gather-on-load)")
-    t_on, gate_up_ms = wb.back_to_back(wb.layer, wb.lora, args.steps, args.warmup, gate_up=True)
+    t_on, _ = wb.back_to_back(wb.layer, wb.lora, args.steps, args.warmup)
     log("timing LoRA off (same kernels, no adapters)")
-    t_off, gate_up_off_ms = wb.back_to_back(wb.layer, None, args.steps, args.warmup, gate_up=True)
+    t_off, _ = wb.back_to_back(wb.layer, None, args.steps, args.warmup)
+    log("timing the gate_up GEMM alone (library-recorded events, separate steps)")
+    _, gate_up_ms = wb.back_to_back(wb.layer, wb.lora, args.steps, 2, gate_up=True)
+    _, gate_up_off_ms = wb.back_to_back(wb.layer, None, args.steps, 2, gate_up=True)
     half = max(5, args.steps // 2)
     log("timing LoRA on with the explicit permute call")
     t_perm = run_only(wb, "explicit-permute", half, 3)["ms_per_step"] * 1e-3
@@ -471,7 +482,8 @@ def main():
     if wb.fp8_ok():
         log("timing LoRA on with FP8 expert weights (E4M3 codes, fp32 scale per 128x128 block)")
         l8, l8p = wb.fp8_layers()
-        t_fp8, fp8_gu = wb.back_to_back(l8, wb.lora, args.steps, args.warmup, gate_up=True)
+        t_fp8, _ = wb.back_to_back(l8, wb.lora, args.steps, args.warmup)
+        _, fp8_gu = wb.back_to_back(l8, wb.lora, half, 2, gate_up=True)
         t_fp8_p2, _ = wb.back_to_back(l8p, wb.lora, half, args.warmup)
         del l8, l8p
         fp8 = (t_fp8, fp8_gu, t_fp8_p2)
