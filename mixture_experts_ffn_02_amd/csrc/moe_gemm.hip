@@ -1344,7 +1344,9 @@ __global__ __launch_bounds__(256) void swiglu_join_kernel(const float *__restric
   *reinterpret_cast<uint2 *>(act + (size_t)p * I + i) = o;
 }
 
-// Library-owned fork/join events, created once per device and reused.
+// Library-owned fork/join events, created once per device and reused.  They order two
+// streams of one device, so they skip the system-scope fence (the release that makes device
+// memory visible to the host), which idles the GPU for microseconds at every record.
 struct StreamEvents {
   hipEvent_t fork = nullptr, ready = nullptr;
 };
@@ -1355,8 +1357,9 @@ int get_events(StreamEvents *&out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ST_HIP;
   if (!created[dev]) {
-    if (hipEventCreateWithFlags(&ev[dev].fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ev[dev].ready, hipEventDisableTiming) != hipSuccess)
+    constexpr unsigned kFlags = hipEventDisableTiming | hipEventDisableSystemFence;
+    if (hipEventCreateWithFlags(&ev[dev].fork, kFlags) != hipSuccess ||
+        hipEventCreateWithFlags(&ev[dev].ready, kFlags) != hipSuccess)
       return ST_HIP;
     created[dev] = 1;
   }
