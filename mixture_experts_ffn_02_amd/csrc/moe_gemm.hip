@@ -236,12 +236,17 @@ void moe_gemm_kernel(const GemmParams P) {
       L_step = (int)gridDim.x;
     }
   } else {
-    // On tile-packed weights the blocks take the tiles in launch order instead: with one
-    // tile per block the weight stream then runs through the packed buffer front to back
-    // (decode gate_up 151 -> 145 us; the XCD-grouped order is the faster one for the
-    // row-major layout, 6.5 against 6.1 TB/s in a streaming probe of the same pattern).
-    L = P.w_packed ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
-    L_end = total;
+    // One tile per block, each XCD a contiguous share of the tiles (consecutive tiles of an
+    // expert share its weights and adapter rows in that XCD's L2).  The shares are cut
+    // from the actual tile count: the grid is only a bound (every expert may add a partial
+    // m-tile), and shares of the bound left the last XCDs without tiles (multi-adapter
+    // T=256: ~190 of 248 m-tiles exist, so two of the eight XCDs idled through the LoRA
+    // shrink; decode on row-major weights, gate_up 146 -> 130 us).  With the shares cut
+    // this way the tile-packed weights stream as fast as in launch order (decode gate_up
+    // 123 us either way).  Blocks past their XCD's share take no tile.
+    const int per_xcd = (total + 7) >> 3, j = (int)(blockIdx.x >> 3);
+    L = (int)(blockIdx.x & 7) * per_xcd + j;
+    L_end = j < per_xcd ? total : 0;
     L_step = 0;
   }
   int parity = 0;
