@@ -128,8 +128,9 @@ typedef struct {
   int32_t packed_weights;
   /* moe_lora_forward_fp8 only: 1 = every block scale is a power of two (as in E8M0 /
    * MX-style scaling), which lets the staging use gfx950's fused scaled FP8 -> bf16
-   * conversion (it applies only the scale's exponent); the result is then identical to
-   * the general path.  0 = arbitrary fp32 scales.  Other values ->
+   * conversion (it applies only the scale's exponent); every weight is then exact in
+   * bf16 and the result has the bits of moe_lora_forward on those dequantized weights.
+   * 0 = arbitrary fp32 scales.  Other values ->
    * MOE_LORA_ERR_INVALID_ARGUMENT; a scale that is not a power of two with 1 set gives
    * wrong weights (the library does not read the scales on the host). */
   int32_t fp8_pow2_scales;
@@ -247,8 +248,11 @@ int moe_lora_forward_noalloc(const moe_lora_dims *dims, const uint16_t *x, const
  *     (sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7f / 0xff are NaN).
  *   w_gate_up_scale [E, 2I/128, H/128], w_down_scale [E, H/128, I/128]: fp32, one scale
  *     per 128 x 128 block; weight = value(code) * scale of its block.
- * Each weight is rounded to bf16 once (fp32 product, round to nearest even) before the
- * bf16 MFMA; everything else is as in moe_lora_forward, whose workspace size applies.
+ * Tiles of up to 64 rows (batches averaging up to 128 routed rows per expert) feed the
+ * codes to the bf16 MFMAs unscaled (every E4M3 value is exact in bf16) and add each
+ * 128-wide K block's fp32 sum times its scale; 128-row tiles round each weight times its
+ * scale to bf16 once (round to nearest even) before the MFMA.  Everything else is as in
+ * moe_lora_forward, whose workspace size applies.
  * All four weight pointers are device pointers, 16-byte aligned (else
  * MOE_LORA_ERR_INVALID_ARGUMENT).  Requires hidden and inter multiples of 128 and at most
  * 8192, and

@@ -107,12 +107,15 @@ struct GemmParams {
   int mt_fast;
 };
 
-// Register budget: two waves per SIMD (256 VGPRs) for every tile height.  Three waves on
-// the 16-row tiles would fit the LDS but cap them at 168 VGPRs, where the four register
-// stages and the LoRA code spill to scratch on every tile (decode gate_up 155 -> 131 us
-// without the cap).
+// Register budget: two waves per SIMD (256 VGPRs), or three (168 VGPRs, as many 16-row
+// blocks as the LDS holds) for the 16-row down tiles and the 16-row FP8 gate_up tiles,
+// which run two register stages at that budget (decode down 72 -> 67.5 us; FP8 gate_up
+// 78 -> 75.6 us, FP8 down 54 -> 51 us).  The bf16 16-row gate_up keeps two waves and four
+// stages: with three it is ~1 % slower, and with four stages at three waves its stages
+// and LoRA code spill to scratch on every tile (155 against 131 us).
 template <int BM, int BN, int WM, int WN, int MODE, int PF, int W8 = 0>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(WM *WN * 64)
+__attribute__((amdgpu_waves_per_eu((BM <= 16 && (MODE == MODE_DOWN || (W8 && MODE == MODE_GATEUP))) ? 3 : 2)))
 void moe_gemm_kernel(const GemmParams P) {
   static_assert(!W8 || MODE == MODE_GATEUP || MODE == MODE_DOWN, "FP8 weights feed the gate_up and down GEMMs");
   constexpr int NT = WM * WN * 64;
@@ -149,6 +152,7 @@ void moe_gemm_kernel(const GemmParams P) {
   // per-lane a is a vector load from the argument block, which waits behind the weight
   // stream)
   __shared__ int s_rank[MOE_LORA_MAX_SLOTS];
+  __shared__ float s_scal[MOE_LORA_MAX_SLOTS];  // and its scaling
   // FP8 weights: the tile's block scales, [2 row blocks][K / 128 <= 64] (gate_up: the gate
   // and the up block of the tile's columns; down: the tile's one or two row blocks)
   __shared__ float s_wsc[W8 ? 2 * 64 : 1];
@@ -185,7 +189,10 @@ void moe_gemm_kernel(const GemmParams P) {
   for (int i = tid; i <= P.E; i += NT) s_off[i] = P.offsets[i];
 #pragma unroll
   for (int s2 = 0; s2 < MOE_LORA_MAX_SLOTS; ++s2)
-    if (tid == s2) s_rank[s2] = P.rank[s2];
+    if (tid == s2) {
+      s_rank[s2] = P.rank[s2];
+      s_scal[s2] = P.scaling[s2];
+    }
   __syncthreads();
   if (wave == 0) {
     const int per = (P.E + 63) / 64;
@@ -388,6 +395,14 @@ void moe_gemm_kernel(const GemmParams P) {
 
   u32x4_t ra[PF][A_IT], rb[PF][B_IT];
   f32x4_t acc[FM][FN];
+  // FP8 weights with general block scales on tiles of up to 64 rows: the codes enter the
+  // MFMAs unscaled (every E4M3 value is exact in bf16), and the sum over each 128-wide K
+  // block is scaled into acc8 when the block's second K step has been computed (w8_kb:
+  // the next block's index).  The 128-row tiles have no registers for a second set of
+  // accumulators and scale each weight before the MFMAs instead.
+  constexpr bool kW8Acc = W8 == 1 && BM <= 64;
+  f32x4_t acc8[kW8Acc ? FM : 1][kW8Acc ? FN : 1];
+  int w8_kb = 0;
 
   auto zero_acc = [&]() {
 #pragma unroll
@@ -462,13 +477,14 @@ void moe_gemm_kernel(const GemmParams P) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) *reinterpret_cast<u32x4_t *>(&As[buf][a_lds[i]]) = xa[i];
     if constexpr (W8) {
-      // 16 E4M3 codes (element j in byte j) -> fp32 (exact) * block scale -> bf16
+      // 16 E4M3 codes (element j in byte j) -> bf16
       const int kb = step >> 1, KB = P.K / 128;
-      if constexpr (W8 == 2) {
-        // power-of-two scales: one fused scaled conversion per two codes (exact)
+      if constexpr (W8 == 2 || kW8Acc) {
+        // one conversion per two codes (exact): scaled by a power-of-two block scale, or
+        // unscaled (see acc8)
 #pragma unroll
         for (int i = 0; i < B8_IT; ++i) {
-          const float sc = s_wsc[b8_sj[i] * KB + kb];
+          const float sc = W8 == 2 ? s_wsc[b8_sj[i] * KB + kb] : 1.0f;
           u32x4_t o[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
@@ -482,6 +498,7 @@ void moe_gemm_kernel(const GemmParams P) {
           *reinterpret_cast<u32x4_t *>(&Bs[buf][b8_lds2[i]]) = o[1];
         }
       } else {
+        // -> fp32 (exact) * block scale -> bf16
 #pragma unroll
         for (int i = 0; i < B8_IT; ++i) {
           const float sc = s_wsc[b8_sj[i] * KB + kb];
@@ -541,6 +558,26 @@ void moe_gemm_kernel(const GemmParams P) {
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32(af[fm], bfr[fn], acc[fm][fn]);
+    }
+  };
+  // FP8 weights, general scales: a 128-wide K block (two K steps) ends, acc8 += block
+  // scale * block sum.  Fragment fn's weight rows lie in one 128-row scale block: gate_up,
+  // the tile's gate block (fn < FN/2) or up block (see brow()); down, the tile's block
+  // holding the fragment's rows
+  auto w8_block_end = [&]() {
+    if constexpr (kW8Acc) {
+      const int KB = P.K / 128;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int j = kGateUp ? fn / (FN / 2) : (wn * WTN + fn * 16) / 128;
+        const float sc = s_wsc[j * KB + w8_kb];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          acc8[fm][fn] += sc * acc[fm][fn];
+          acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      ++w8_kb;
     }
   };
 
@@ -624,9 +661,9 @@ void moe_gemm_kernel(const GemmParams P) {
       const int r = c / cpr, ch = c % cpr, j0 = ch * 8;
       const int a = s_slot[r];
       u32x4_t v4 = zero_u32x4();
-      // The chunk test reads the rank from the LDS table, so that the partial loads do not
-      // wait for a load of it: the rank and scaling loads below (vector loads, a is per
-      // lane) travel with them, one round trip instead of two.
+      // Rank and scaling come from the LDS tables (a is per lane: indexing the argument
+      // block with it made the compiler copy the whole block to scratch memory in some
+      // instantiations), so the partial loads wait for no other load.
       if (a >= 0 && j0 < s_rank[a]) {
         const f32x4_t *src = reinterpret_cast<const f32x4_t *>(P.part + (size_t)(row0 + r) * P.rmax + j0);
         const size_t split_stride = (size_t)P.R * P.rmax / 4;  // in f32x4 units
@@ -649,8 +686,8 @@ void moe_gemm_kernel(const GemmParams P) {
               v[4 + t] += x[q][1][t];
             }
         }
-        const int ra_rank = P.rank[a];
-        const float sc = P.scaling[a];
+        const int ra_rank = s_rank[a];
+        const float sc = s_scal[a];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float lo = (j0 + 2 * q < ra_rank) ? v[2 * q] * sc : 0.f;
@@ -682,6 +719,7 @@ void moe_gemm_kernel(const GemmParams P) {
         for (int u = 0; u < PF; ++u) {
           load_full((s_begin + i + u + PF) * BK, bbase, bcount, ra[u], rb[u], nt, pk);
           compute(u & 1);
+          if (u & 1) w8_block_end();  // (FP8: the main loop starts at K step 0, PF is even)
           store_lds((u + 1) & 1, ra[(u + 1) % PF], rb[(u + 1) % PF], s_begin + i + u + 1);
           __syncthreads();
         }
@@ -690,6 +728,7 @@ void moe_gemm_kernel(const GemmParams P) {
       for (int u = 0; u < PF; ++u) {
         tail_load(u);
         compute(u & 1);
+        if (u & 1) w8_block_end();
         if (u + 1 < PF) store_lds((u + 1) & 1, ra[u + 1], rb[u + 1], s_begin + n_main - PF + u + 1);
         __syncthreads();
       }
@@ -701,6 +740,7 @@ void moe_gemm_kernel(const GemmParams P) {
       store_lds(0, ra[0], rb[0], s);
       __syncthreads();
       compute(0);
+      if (s & 1) w8_block_end();
       __syncthreads();
     }
   };
@@ -902,6 +942,13 @@ void moe_gemm_kernel(const GemmParams P) {
       }
       main_loop(nt, std::false_type{});
     };
+    if constexpr (kW8Acc) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc8[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      w8_kb = 0;
+    }
     if (kHasMain) {
       if constexpr (kStreamB) {
         if (single_mtile)
@@ -913,6 +960,13 @@ void moe_gemm_kernel(const GemmParams P) {
       }
     } else {
       build();
+    }
+    if constexpr (kW8Acc) {
+      // (K is a multiple of 128 with FP8 weights: the last block was scaled in)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = acc8[fm][fn];
     }
     if (kExtLds && ext_lds) {
       // one K step over ranks 0-31: A fragments from Xs (rows of other slots or none are
@@ -1245,12 +1299,12 @@ int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
   const int BN = 128;
   const int ncols = (MODE == MODE_GATEUP) ? cdiv(P.I, BN / 2) : cdiv(P.N, BN);
   switch (bm) {
-    // FP8 weights: a K step carries half the bytes, so the down tiles keep six steps in
-    // flight; gate_up keeps four, where more stages measured slower (the conversion of
-    // the codes, not the loads, sets its pace); both divide the decode K of 2048 and 768
+    // Register stages of the 16-row tiles: two where three waves share a SIMD (see the
+    // kernel's register budget), four on the bf16 gate_up (FP8 gate_up at two waves: four,
+    // six and eight stages measured 76, 82 and 80 us)
     case 16:
-      if constexpr (W8) return launch_cfg<16, 128, 1, 4, MODE, MODE == MODE_GATEUP ? 4 : 6, W8>(P, ncols, s);
-      else return launch_cfg<16, 128, 1, 4, MODE, 4>(P, ncols, s);
+      if constexpr (W8) return launch_cfg<16, 128, 1, 4, MODE, 2, W8>(P, ncols, s);
+      else return launch_cfg<16, 128, 1, 4, MODE, MODE == MODE_DOWN ? 2 : 4>(P, ncols, s);
     case 64: return launch_cfg<64, 128, 2, 2, MODE, 2, W8>(P, ncols, s);
     default: return launch_cfg<128, 256, 4, 2, MODE, 2, W8>(P, (MODE == MODE_GATEUP) ? cdiv(P.I, 128) : cdiv(P.N, 256), s);
   }

@@ -3,7 +3,10 @@
 Parity: the layer on E4M3 codes with 128 x 128 fp32 block scales against the fp64 oracle
 on the dequantized weights (tile heights 16, 64 and 128 with LoRA; decode without LoRA).
 Bit identity: with power-of-two block scales every dequantized weight is exact in bf16,
-so the FP8 kernels must give the same bits as the bf16 kernels run on those bf16 weights.
+so the path that scales each weight in its conversion (opts.fp8_pow2_scales, and the
+general path on 128-row tiles) must give the same bits as the bf16 kernels run on those
+bf16 weights.  The general path on tiles of up to 64 rows scales the fp32 sum of each
+128-wide K block instead (a different rounding order): held to the oracle's bar.
 Code range: one case draws every finite E4M3 code (+-0, the subnormals, up to +-448), so
 the hardware conversions (the general one and the fused scaled one) meet all of them.
 """
@@ -98,15 +101,20 @@ def test_fp8_pow2_scales_bit_identical_to_bf16_kernels(cfg):
     say(f"[fp8 vs bf16] {cfg.name}")
     case = Fp8Case(cfg, pow2=True)
     out8 = case.run()
-    # the fused scaled conversion (opts.fp8_pow2_scales) gives the same bits
-    assert torch.equal(case.run(pow2_path=True, packed=ml.PACKED_GATE_UP | ml.PACKED_DOWN), out8)
+    # the fused scaled conversion (opts.fp8_pow2_scales) gives the bf16 kernels' bits
+    out_p2 = case.run(pow2_path=True, packed=ml.PACKED_GATE_UP | ml.PACKED_DOWN)
     c, g = case.cfg, case.g
     layer16 = ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, _bf16_from_dequant(case, 1),
                               _bf16_from_dequant(case, 2), g.routing, c.n_group, c.topk_group,
                               c.routed_scaling_factor, g.bias)
     out16 = layer16(g.x, g.logits, g.lora_slots())
     torch.cuda.synchronize()
-    assert torch.equal(out8, out16)
+    assert torch.equal(out_p2, out16)
+    # the general path: per-weight scaling on 128-row tiles gives the same bits, block-sum
+    # scaling on shorter tiles stays within the oracle's bar
+    if cfg is TALL8:
+        assert torch.equal(out8, out16)
+    assert_layer_close(f64(out8), case.oracle()["out"], f"fp8 general path, pow2 scales {cfg.name}")
 
 
 @pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], MID8, TALL8],
@@ -127,7 +135,8 @@ FINITE_E4M3 = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=n
 def test_fp8_every_finite_code(cfg):
     """Weights whose codes span every finite E4M3 value: the general conversion (arbitrary
     scales) within the bar of the oracle; with power-of-two scales both conversions within
-    the bar and bit-identical to the bf16 kernels on the exactly dequantized weights."""
+    the bar, and the scaled conversion bit-identical to the bf16 kernels on the exactly
+    dequantized weights."""
     say(f"[fp8 full code range] {cfg.name}")
     case = Fp8Case(cfg, full_range=True)
     for codes in (case.c1, case.c2):
@@ -137,14 +146,15 @@ def test_fp8_every_finite_code(cfg):
     ref = case2.oracle()["out"]
     out8 = case2.run()
     assert_layer_close(f64(out8), ref, f"fp8 all codes pow2 scales {cfg.name}")
-    assert torch.equal(case2.run(pow2_path=True, packed=ml.PACKED_GATE_UP | ml.PACKED_DOWN), out8)
+    out_p2 = case2.run(pow2_path=True, packed=ml.PACKED_GATE_UP | ml.PACKED_DOWN)
+    assert_layer_close(f64(out_p2), ref, f"fp8 all codes pow2 path {cfg.name}")
     c, g = case2.cfg, case2.g
     layer16 = ml.MoELoRALayer(c.H, c.I, c.E, c.top_k, _bf16_from_dequant(case2, 1),
                               _bf16_from_dequant(case2, 2), g.routing, c.n_group, c.topk_group,
                               c.routed_scaling_factor, g.bias)
     out16 = layer16(g.x, g.logits, g.lora_slots())
     torch.cuda.synchronize()
-    assert torch.equal(out8, out16)
+    assert torch.equal(out_p2, out16)
 
 
 def test_fp8_with_side_stream_runs_the_fused_path():
