@@ -1235,13 +1235,15 @@ int shrink_bm(int R, int E) {
   return avg <= 16 ? 16 : (avg <= 48 ? 32 : 128);
 }
 
-// Split K so that the grid has ~1024 workgroups, each with at least 4 pipelined K steps.
+// Split K so that the grid has ~512 workgroups, each with at least 4 pipelined K steps
+// (against ~1024: multi-adapter T=256 shrink 18.1 -> 15.7 us per launch, DeepSeek-V3-sized
+// 27.9 -> 26.0 us, decode even; ~256 was slower at decode and DeepSeek-V3 sizes).
 // With several adapter slots each (m-tile, split) gets one block per slot (slot groups),
 // so the slots' passes over K run side by side instead of one after another in a block.
 int shrink_splits(int R, int E, int K, int groups, int &steps_per_split) {
   const int steps = cdiv(K, BK);
   const int tiles = mtile_bound(R, E, shrink_bm(R, E)) * (groups > 1 ? groups : 1);
-  int want = cdiv(1024, tiles > 0 ? tiles : 1);
+  int want = cdiv(512, tiles > 0 ? tiles : 1);
   if (want < 1) want = 1;
   steps_per_split = cdiv(steps, want);
   if (steps_per_split < 4) steps_per_split = steps < 4 ? steps : 4;
