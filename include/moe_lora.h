@@ -228,9 +228,9 @@ int moe_lora_forward(const moe_lora_dims *dims, const uint16_t *x, const uint16_
  *   Returns MOE_LORA_ERR_SCRATCH_TOO_SMALL, enqueuing nothing, when the problem's fused
  *   workspace (moe_lora_forward_workspace_size without the decomposed path's buffers)
  *   exceeds the scratch: the decode-sized batches fit (64 tokens of a hidden-2048,
- *   128-expert, top-8 layer with a rank-16 adapter need ~1.4 MiB; 256 tokens with four
- *   adapters up to rank 64 ~10 MiB); 8192-token prefill batches of that layer (154 MiB)
- *   and 1024 tokens of a hidden-7168, 256-expert layer (68 MiB) do not.
+ *   128-expert, top-8 layer with a rank-16 adapter need ~1.3 MiB; 256 tokens with four
+ *   adapters up to rank 64 ~10 MiB); 8192-token prefill batches of that layer (150 MiB)
+ *   and 1024 tokens of a hidden-7168, 256-expert layer (67 MiB) do not.
  * Concurrency: every call on one GPU uses the same scratch, which keeps the last call's
  * contents (nothing in it needs to start at zero).  Calls that overlap on one GPU, from
  * several host threads or on several streams without ordering between them, race on it

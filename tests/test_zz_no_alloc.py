@@ -71,7 +71,7 @@ def test_noalloc_forward_equals_forward_on_two_calls():
 
 
 def test_noalloc_forward_refuses_what_does_not_fit():
-    cfg = NAMED_CONFIGS[3]  # 8192 tokens: a 154 MiB fused workspace
+    cfg = NAMED_CONFIGS[3]  # 8192 tokens: a 150 MiB fused workspace
     say(f"[noalloc limits] {cfg.name}")
     g = GpuLayer(Workload(cfg, 0))
     layer = g.layer()
