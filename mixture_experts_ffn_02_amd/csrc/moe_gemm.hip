@@ -610,12 +610,13 @@ void moe_gemm_kernel(const GemmParams P) {
     for (int i = 0; i < B_IT; ++i) *reinterpret_cast<u32x4_t *>(&Bs[buf][b_lds[i]]) = xb[i];
   };
   // one 64-wide K step of the expand: A rows from Xs masked to the rows of slot a
-  // (ranks past rmax are zero in Xs, so the second 32-wide half is skipped when rmax <= 32;
+  // (a row's ranks past its own slot's are zero in Xs, so the second 32-wide half is
+  // skipped when slot a's rank is at most 32: multi-adapter gate_up 143.4 -> 141.0 us;
   // with one slot in the tile, rows of no slot are zero in Xs and need no mask)
   auto compute_ext = [&](int buf, int a, bool masked) {
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
-      if (kk > 0 && P.rmax <= 32) break;
+      if (kk > 0 && (P.rmax <= 32 || P.rank[a] <= 32)) break;
       u32x4_t af[FM], bfr[FN];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
