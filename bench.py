@@ -82,7 +82,7 @@ def committed_traffic(workload: str):
     except Exception:
         return None
     rec = d.get(workload)
-    if not rec or rec.get("moe_gemm_sha") != kernel_source_hash():
+    if not rec or d.get("moe_gemm_sha") != kernel_source_hash():
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -274,6 +274,7 @@ class Workbench:
         r["kernel_avg_us"] = round(gate_up_ms * 1e3, 2)
         r["algorithmic_bytes_per_launch"] = int(c["gate_up_bytes"])
         r["algorithmic_flops_per_launch"] = int(c["gate_up_flops"])
+        r["traffic"] = committed_traffic(self.cfg.name)
         return r
 
     def layer_roofline(self, c, step_s):
