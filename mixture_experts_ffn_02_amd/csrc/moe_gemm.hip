@@ -74,7 +74,7 @@ struct GemmParams {
   int E, top_k, R;
   int n_cols;  // n-tiles (GEMM modes) or K splits x slot groups (SHRINK)
   int k_steps_per_split;
-  int slot_groups;  // SHRINK: blocks per (m-tile, K split); group g takes slots g, g + groups, ...
+  int slot_groups;  // SHRINK: blocks per (m-tile, K split), one per BN-wide chunk of each slot's ranks
   int num_slots;
   const int32_t *token_slot;
   int rank[MOE_LORA_MAX_SLOTS];
@@ -762,16 +762,23 @@ void moe_gemm_kernel(const GemmParams P) {
     const int s0 = split * P.k_steps_per_split;
     const int s1 = min(steps_total, s0 + P.k_steps_per_split);
     const int s1f = min(s1, full_total);
-    for (int a = col % groups; a < P.num_slots; a += groups) {
-      if (!((slot_mask >> a) & 1)) continue;
-      const int r_a = P.rank[a];
-      const uint16_t *bbase = P.lora_w[a] + (size_t)(P.lora_w_shared ? 0 : e) * r_a * P.K;
+    // group g: chunk c of slot a's rank columns [c BN, c BN + BN), the groups enumerating
+    // the slots in order with ceil(rank / BN) chunks each
+    int a = 0, c = col % groups;
+    while (a < P.num_slots && c >= (P.rank[a] + BN - 1) / BN) {
+      c -= (P.rank[a] + BN - 1) / BN;
+      ++a;
+    }
+    if (a < P.num_slots && ((slot_mask >> a) & 1)) {
+      const int r_a = P.rank[a], c0 = c * BN;
+      const int rc = min(BN, r_a - c0);  // rank rows of this chunk
+      const uint16_t *bbase = P.lora_w[a] + ((size_t)(P.lora_w_shared ? 0 : e) * r_a + c0) * P.K;
       zero_acc();
-      run_full(s0, s1f, bbase, r_a, [] {}, [](int) {}, std::false_type{}, std::false_type{});
+      run_full(s0, s1f, bbase, rc, [] {}, [](int) {}, std::false_type{}, std::false_type{});
       if (s1 > s1f) run_single([&](u32x4_t(&xa)[A_IT], u32x4_t(&xb)[B_IT]) {
-        load_tail(s1f * BK, bbase, r_a, xa, xb);
+        load_tail(s1f * BK, bbase, rc, xa, xb);
       });
-      // rows of this slot, rank columns
+      // rows of this slot, the chunk's rank columns
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -780,8 +787,8 @@ void moe_gemm_kernel(const GemmParams P) {
           for (int i = 0; i < 4; ++i) {
             const int r = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
             const int n = wn * WTN + fn * 16 + (lane & 15);
-            if (r < rows && n < r_a && s_slot[r] == a)
-              P.out_f32[((size_t)split * P.R + row0 + r) * P.rmax + n] = acc[fm][fn][i];
+            if (r < rows && n < rc && s_slot[r] == a)
+              P.out_f32[((size_t)split * P.R + row0 + r) * P.rmax + c0 + n] = acc[fm][fn][i];
           }
     }
   } else {
@@ -1251,6 +1258,18 @@ int shrink_splits(int R, int E, int K, int groups, int &steps_per_split) {
   return cdiv(steps, steps_per_split);
 }
 
+// Rank columns per LoRA shrink tile: 32 on the 16- and 32-row tiles (a slot of higher rank
+// takes several column chunks, each its own block), and on the 128-row tiles when every
+// rank fits them; else 64
+int shrink_bn(int bm, int rmax) { return (bm <= 32 || rmax <= 32) ? 32 : 64; }
+
+// blocks per (m-tile, K split) of the LoRA shrink: one per shrink_bn-wide chunk of each slot
+int shrink_groups(const int *rank, int num_slots, int bn) {
+  int g = 0;
+  for (int s = 0; s < num_slots; ++s) g += (rank[s] + bn - 1) / bn;
+  return g > 0 ? g : 1;
+}
+
 int rmax8(const moe_lora_adapters *lora) {
   int r = 0;
   for (int s = 0; s < lora->num_slots; ++s) r = lora->rank[s] > r ? lora->rank[s] : r;
@@ -1315,17 +1334,16 @@ int launch_gemm(const GemmParams &P, int bm, hipStream_t s) {
 
 int launch_shrink(const GemmParams &P0, int bm, int splits, hipStream_t s) {
   GemmParams P = P0;
-  P.slot_groups = P.num_slots > 1 ? P.num_slots : 1;
+  const int bn = shrink_bn(bm, P.rmax);
+  P.slot_groups = shrink_groups(P.rank, P.num_slots, bn);
   const int cols = splits * P.slot_groups;
-  // 32 rank columns when every slot fits them: a 64-wide tile spends most of its B loads
-  // on clamped rows past the rank (decode -0.6 %, prefill -0.4 %)
-  if (P.rmax <= 32) {
-    if (bm <= 16) return launch_cfg<16, 32, 1, 2, MODE_SHRINK, 2>(P, cols, s);
-    if (bm <= 32) return launch_cfg<32, 32, 2, 1, MODE_SHRINK, 2>(P, cols, s);
-    return launch_cfg<128, 32, 4, 1, MODE_SHRINK, 2>(P, cols, s);
-  }
-  if (bm <= 16) return launch_cfg<16, 64, 1, 4, MODE_SHRINK, 2>(P, cols, s);
-  if (bm <= 32) return launch_cfg<32, 64, 2, 2, MODE_SHRINK, 2>(P, cols, s);
+  // 32 rank columns per block: a 64-wide tile spent most of its B loads on clamped rows
+  // past small ranks (decode -0.6 %, prefill -0.4 %), and on the short tiles it stages
+  // twice the LDS bytes per K step for the same rows, where the LDS-staged K step (not the
+  // loads) bounds the launch; 128-row tiles keep 64 columns for ranks above 32
+  if (bm <= 16) return launch_cfg<16, 32, 1, 2, MODE_SHRINK, 2>(P, cols, s);
+  if (bm <= 32) return launch_cfg<32, 32, 2, 1, MODE_SHRINK, 2>(P, cols, s);
+  if (bn == 32) return launch_cfg<128, 32, 4, 1, MODE_SHRINK, 2>(P, cols, s);
   return launch_cfg<128, 64, 2, 2, MODE_SHRINK, 2>(P, cols, s);
 }
 
@@ -1453,8 +1471,9 @@ FwdLayout layout(const moe_lora_dims &d, const moe_lora_adapters *lora, bool fus
   size_t off = 0;
   if (has_lora) {
     L.rmax = rmax8(lora);
-    L.splits1 = shrink_splits((int)R, d.num_experts, d.hidden, lora->num_slots, L.steps1);
-    L.shrink2_splits = shrink_splits((int)R, d.num_experts, d.inter, lora->num_slots, L.steps2);
+    const int groups = shrink_groups(lora->rank, lora->num_slots, shrink_bn(shrink_bm((int)R, d.num_experts), L.rmax));
+    L.splits1 = shrink_splits((int)R, d.num_experts, d.hidden, groups, L.steps1);
+    L.shrink2_splits = shrink_splits((int)R, d.num_experts, d.inter, groups, L.steps2);
     // the fused path writes one down-shrink partial per gate_up n-tile (64 or 128 I columns)
     L.splits2 = L.shrink2_splits > cdiv(d.inter, 64) ? L.shrink2_splits : cdiv(d.inter, 64);
     L.u_part = off;
