@@ -26,6 +26,9 @@ MID8 = make_config(name="fp8_mid_T512_H512_I256_E32_k8", cfg_id=212, T=512, H=51
                    slots=((32, 1.0), (16, 2.0), (8, 0.5)), slot_assignment="uniform")
 TALL8 = make_config(name="fp8_tall_T1024_H256_I256_E8_k2", cfg_id=213, T=1024, H=256, I=256, E=8, top_k=2,
                     slots=((16, 2.0),))
+# 16 rows per expert on average: 32-row gate_up tiles, 64-row down tiles
+SHORT8 = make_config(name="fp8_short_T64_H512_I256_E32_k8", cfg_id=214, T=64, H=512, I=256, E=32, top_k=8,
+                     slots=((16, 2.0), (32, 1.0)), slot_assignment="uniform")
 
 
 def _stack(fn, E):
@@ -77,8 +80,8 @@ class Fp8Case:
 
 
 @pytest.mark.parametrize("cfg,with_lora", [(NAMED_CONFIGS[1], True), (NAMED_CONFIGS[2], True),
-                                           (NAMED_CONFIGS[2], False), (MID8, True), (TALL8, True)],
-                         ids=["tiny", "decode", "decode-base", "mid-64row", "tall-128row"])
+                                           (NAMED_CONFIGS[2], False), (SHORT8, True), (MID8, True), (TALL8, True)],
+                         ids=["tiny", "decode", "decode-base", "short-32row", "mid-64row", "tall-128row"])
 def test_fp8_layer_parity(cfg, with_lora):
     say(f"[fp8] {cfg.name} lora={with_lora}")
     case = Fp8Case(cfg)
@@ -117,8 +120,8 @@ def test_fp8_pow2_scales_bit_identical_to_bf16_kernels(cfg):
     assert_layer_close(f64(out8), case.oracle()["out"], f"fp8 general path, pow2 scales {cfg.name}")
 
 
-@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], MID8, TALL8],
-                         ids=["tiny", "decode", "mid-64row", "tall-128row"])
+@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], SHORT8, MID8, TALL8],
+                         ids=["tiny", "decode", "short-32row", "mid-64row", "tall-128row"])
 def test_fp8_packed_layouts_bit_identical(cfg):
     """The FP8 tile-packed layout (each weight alone and both) only reorders the codes."""
     say(f"[fp8 packed] {cfg.name}")
