@@ -174,8 +174,9 @@ void moe_gemm_kernel(const GemmParams P) {
   // ranks per row, 16-byte chunks XOR-swizzled by row / 4), so the expand is one unmasked
   // 32-wide K step from LDS instead of a register-staged step that waits for its loads
   // at the end of the tile.  Decode-height tiles and the 64-row down GEMM have the LDS
-  // for it (on the 128x256 down tile the extra addressing spilled in the K loop).
-  constexpr bool kExtLds = kHasExt && kHasMain && (BM <= 16 || (MODE == MODE_DOWN && BM <= 64));
+  // for it (on the 128x256 down tile the extra addressing spilled in the K loop; the
+  // 32-row down tile fits three blocks per CU only without it).
+  constexpr bool kExtLds = kHasExt && kHasMain && (BM <= 16 || (MODE == MODE_DOWN && BM == 64));
   constexpr int kEbRank = 32;
   static_assert(!kExtLds || (BN * kEbRank / 8) % 64 == 0, "expand B region must be whole wave copies");
   __shared__ __attribute__((aligned(16))) uint16_t Eb[kExtLds ? BN * kEbRank : 8];
@@ -1546,13 +1547,13 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   const uint16_t *a_src = x_perm ? x_perm : x;
   const int a_gather = x_perm ? 0 : 1;
   const int bm = pick_bm(R, d.num_experts);
-  // The gate_up GEMM of batches with up to 16 rows per expert on average takes 32-row tiles
-  // (one tile per block, three blocks per CU; an expert rarely has more than 32 rows, so
-  // its weights are still read once), where the 64-row tile was three quarters padding;
-  // the down GEMM keeps its 64-row tiles (the 32-row down tile measured slower) and the
-  // separate down shrink.  Multi-adapter T=256: gate_up 143.5 -> 130.9 us with LoRA,
-  // 129.4 -> 123.0 us without.
-  const int bm_gu = (bm == 64 && R <= 16 * d.num_experts) ? 32 : bm;
+  // Batches with up to 16 rows per expert on average run both GEMMs on 32-row tiles (one
+  // tile per block, three blocks per CU; an expert rarely has more than 32 rows, so its
+  // weights are still read once), where the 64-row tile was three quarters padding; the
+  // down-LoRA shrink stays a launch of its own, as for 64-row tiles.  Multi-adapter T=256:
+  // gate_up 143.5 -> 130.9 us with LoRA, 129.4 -> 123.0 us without; down 90.8 -> 85.7 us
+  // and 74.9 -> 72.6 us.
+  const int bm_gemm = (bm == 64 && R <= 16 * d.num_experts) ? 32 : bm;
   int st;
 
   hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->gate_up_event_begin) : nullptr;
@@ -1600,7 +1601,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   // 1.86 ms; multi-adapter even) and the 128-row down tiles (prefill: 0.91 -> 0.73 GB,
   // 380 -> 363 us); column first elsewhere (the 64-row down tiles read 0.9 GB less but took
   // 1.10 -> 1.15 ms; 128-row gate_up 568 -> 575 us)
-  gu.mt_fast = (bm_gu == 64);
+  gu.mt_fast = (bm_gemm == 64);
 
   if (!decomposed) {
     // fused: shrink, then the GEMM appends the LoRA expand as extra K steps and applies
@@ -1618,7 +1619,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       gu.down_part = v_part;
     }
     if (ev0 && hipEventRecord(ev0, main) != hipSuccess) return ST_HIP;
-    if ((st = fp8 ? (pow2 ? launch_gemm<MODE_GATEUP, 2>(gu, bm_gu, main) : launch_gemm<MODE_GATEUP, 1>(gu, bm_gu, main)) : launch_gemm<MODE_GATEUP>(gu, bm_gu, main)) !=
+    if ((st = fp8 ? (pow2 ? launch_gemm<MODE_GATEUP, 2>(gu, bm_gemm, main) : launch_gemm<MODE_GATEUP, 1>(gu, bm_gemm, main)) : launch_gemm<MODE_GATEUP>(gu, bm_gemm, main)) !=
         ST_OK)
       return st;
     if (ev1 && hipEventRecord(ev1, main) != hipSuccess) return ST_HIP;
@@ -1707,7 +1708,7 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
       }
     }
     P.out_bf16 = y_perm;
-    if ((st = fp8 ? (pow2 ? launch_gemm<MODE_DOWN, 2>(P, bm, main) : launch_gemm<MODE_DOWN, 1>(P, bm, main)) : launch_gemm<MODE_DOWN>(P, bm, main)) != ST_OK)
+    if ((st = fp8 ? (pow2 ? launch_gemm<MODE_DOWN, 2>(P, bm_gemm, main) : launch_gemm<MODE_DOWN, 1>(P, bm_gemm, main)) : launch_gemm<MODE_DOWN>(P, bm_gemm, main)) != ST_OK)
       return st;
   }
   return ST_OK;
