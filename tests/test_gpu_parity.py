@@ -367,10 +367,18 @@ WIDE = make_config(name="wide_T48_H256_I128_E8_k2_6slots", cfg_id=203, T=48, H=2
                    slot_assignment="uniform")
 
 
-@pytest.mark.parametrize("cfg", [MID, WIDE], ids=lambda c: c.name)
+# ~15 rows per expert (32-row GEMM tiles) with ragged K (hidden 200, inter 88), a rank-64
+# slot (two 32-column LoRA shrink chunks) and a rank that is not a multiple of 8
+SHORT_RAGGED = make_config(name="short_ragged_T40_H200_I88_E8_k3", cfg_id=215, T=40, H=200, I=88, E=8, top_k=3,
+                           slots=((64, 0.5), (13, 1.0), (8, 2.0)), slot_assignment="uniform",
+                           w_std=0.05, lora_a_std=0.1, lora_b_std=0.1)
+
+
+@pytest.mark.parametrize("cfg", [MID, WIDE, SHORT_RAGGED], ids=lambda c: c.name)
 def test_layer_parity_tile_shapes(cfg):
-    """64-row tiles with three adapter slots, and six slots up to rank 64 (the shrink and
-    expand loops over many slots and uneven ranks)."""
+    """64-row tiles with three adapter slots, six slots up to rank 64 on 32-row tiles (the
+    shrink and expand loops over many slots and uneven ranks), and 32-row tiles with ragged K
+    and a rank-64 slot."""
     g = gpu_layer(cfg)
     say(f"[layer] {cfg.name}")
     _, _, out = _layer_case(g)
