@@ -250,6 +250,8 @@ class Workbench:
             "active_experts": active,
             "layer_bytes": w_gu + w_dn + lora_all + io,
             "layer_flops": 2 * R * 3 * I * H + lora_flops,
+            "layer_bytes_no_lora": w_gu + w_dn + io,
+            "layer_flops_no_lora": 2 * R * 3 * I * H,
             "gate_up_bytes": w_gu + lora_gu + T * H * 2 + R * I * 2,
             # FP8 weights: one byte per weight plus one fp32 scale per 128 x 128 block
             "gate_up_bytes_fp8": (active * 2 * I * H + active * (2 * I // 128) * (H // 128) * 4 + lora_gu
@@ -278,10 +280,15 @@ class Workbench:
         return r
 
     def layer_roofline(self, c, step_s):
+        # the LoRA ratio a layer at its bound could reach: no-LoRA over LoRA-on bytes (HBM
+        # bound) or flops (MFMA bound) of the same step
+        nl, wl = (("layer_bytes_no_lora", "layer_bytes") if c["bound"] == "hbm"
+                  else ("layer_flops_no_lora", "layer_flops"))
         return {"algorithmic_bytes": int(c["layer_bytes"]), "algorithmic_flops": int(c["layer_flops"]),
                 "active_experts": c["active_experts"],
                 "hbm_frac": round(c["layer_bytes"] / step_s / (HBM_PEAK_GBS * 1e9), 4),
-                "mfma_frac": round(c["layer_flops"] / step_s / (BF16_PEAK_TFLOPS * 1e12), 4)}
+                "mfma_frac": round(c["layer_flops"] / step_s / (BF16_PEAK_TFLOPS * 1e12), 4),
+                "lora_ratio_at_bound": round(c[nl] / c[wl], 4)}
 
     def fp8_layers(self):
         """The same workload's expert weights as E4M3 codes with fp32 128 x 128 block scales
