@@ -1230,8 +1230,9 @@ int mtile_bound(int R, int E, int BM) {
 
 // Tile height from the mean rows per expert (the routed load is only known on device).
 // Above 8 rows the 64-row tile keeps most experts in one m-tile, so each weight row is
-// streamed from HBM once (tiles of 16 or 32 rows re-read the weights of every expert
-// with more rows: 1.2x slower at 16 rows per expert, 1.7x on a DeepSeek-V3-sized layer).
+// streamed from HBM once (16-row tiles re-read the weights of every expert with more
+// rows: 1.2x slower at 16 rows per expert, 1.7x on a DeepSeek-V3-sized layer; the GEMMs
+// of batches up to 16 rows per expert then run 32-row tiles, see launch_forward).
 int pick_bm(int R, int E) {
   const int avg = R / (E > 0 ? E : 1);
   if (avg <= 8) return 16;
@@ -1247,8 +1248,9 @@ int shrink_bm(int R, int E) {
 // Split K so that the grid has ~512 workgroups, each with at least 4 pipelined K steps
 // (against ~1024: multi-adapter T=256 shrink 18.1 -> 15.7 us per launch, DeepSeek-V3-sized
 // 27.9 -> 26.0 us, decode even; ~256 was slower at decode and DeepSeek-V3 sizes).
-// With several adapter slots each (m-tile, split) gets one block per slot (slot groups),
-// so the slots' passes over K run side by side instead of one after another in a block.
+// Each (m-tile, split) gets one block per rank-column chunk of each adapter slot (the
+// groups of shrink_groups), so the slots' passes over K run side by side instead of one
+// after another in a block.
 int shrink_splits(int R, int E, int K, int groups, int &steps_per_split) {
   const int steps = cdiv(K, BK);
   const int tiles = mtile_bound(R, E, shrink_bm(R, E)) * (groups > 1 ? groups : 1);
