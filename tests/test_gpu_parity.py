@@ -319,6 +319,45 @@ def test_layer_parity_dsv3_full_weights_every_token():
     torch.cuda.empty_cache()
 
 
+# the largest batch one routing call accepts for 128 experts at top-8 (256 workgroups of 256
+# tokens): 524288 routed rows, so the permuted down output alone is 2 GiB
+MAX_T = make_config(name="maxtok_T65536_H2048_I768_E128_k8_r16", cfg_id=216, T=65536, H=2048, I=768, E=128,
+                    top_k=8, slots=((16, 2.0),))
+
+
+@pytest.mark.timeout(600)
+def test_layer_parity_at_the_routing_token_limit():
+    """A full layer at the routing call's token limit (128-row persistent tiles, row offsets
+    past 2^31 bytes in the permuted buffers): routing of every token bit-exact, the outputs
+    of 257 tokens spread over the batch within the bar, and the tile-packed weights giving
+    the same bits."""
+    cfg = MAX_T
+    _CACHE.clear()
+    torch.cuda.empty_cache()
+    say(f"[layer] {cfg.name}: routing limit")
+    g = GpuLayer(Workload(cfg, 0), stream_weights=True)
+    layer, lora, out = _layer_case(g)
+    rt = _route_of(layer, cfg.T, lora)
+    ref_ids, ref_w = oracle.route(g.logits_np, cfg.top_k, cfg.routing, g.bias_np, cfg.n_group, cfg.topk_group,
+                                  cfg.routed_scaling_factor)
+    check_route(rt, ref_ids, ref_w, cfg.E)
+    assert cfg.R * cfg.H * 2 >= 1 << 31
+    packed = g.packed_layer(ml.PACKED_GATE_UP | ml.PACKED_DOWN)
+    out_p = packed(g.x, g.logits, lora).clone()
+    torch.cuda.synchronize()
+    del packed
+    assert torch.equal(out, out_p), "tile-packed weights changed the output"
+    idx = np.r_[np.arange(0, cfg.T, 257), cfg.T - 1]
+    say(f"  oracle on {len(idx)} tokens")
+    ref = oracle.layer(g.x_np[idx], g.logits_np[idx], cfg.top_k, cfg.I, g.w_gate_up, g.w_down,
+                       g.oracle_adapters(), g.slots_np[idx], cfg.routing, g.bias_np, cfg.n_group,
+                       cfg.topk_group, cfg.routed_scaling_factor, num_experts=cfg.E)
+    np.testing.assert_array_equal(ref["ids"], ref_ids[idx])
+    assert_layer_close(f64(out[idx]), ref["out"], "routing-limit batch, sampled tokens")
+    del g
+    torch.cuda.empty_cache()
+
+
 def test_empty_batch():
     g = gpu_layer(NAMED_CONFIGS[1])
     c = g.cfg
