@@ -1554,7 +1554,8 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
   // weights are still read once), where the 64-row tile was three quarters padding; the
   // down-LoRA shrink stays a launch of its own, as for 64-row tiles.  Multi-adapter T=256:
   // gate_up 143.5 -> 130.9 us with LoRA, 129.4 -> 123.0 us without; down 90.8 -> 85.7 us
-  // and 74.9 -> 72.6 us.
+  // and 74.9 -> 72.6 us.  The decomposed path's fp32 gate_up and LoRA expand take the same
+  // tiles (its two-stream step 303 -> 287 us).
   const int bm_gemm = (bm == 64 && R <= 16 * d.num_experts) ? 32 : bm;
   int st;
 
@@ -1647,12 +1648,12 @@ int launch_forward(const moe_lora_dims &d, const uint16_t *x, const uint16_t *x_
     ex.part_splits = L.splits1;
     ex.row_slot = row_slot;
     ex.out_f32 = Db;
-    if ((st = launch_gemm<MODE_EXPAND_F32>(ex, bm, lora_stream)) != ST_OK) return st;
+    if ((st = launch_gemm<MODE_EXPAND_F32>(ex, bm_gemm, lora_stream)) != ST_OK) return st;
     if (lora_stream != main && hipEventRecord(sev->ready, lora_stream) != hipSuccess) return ST_HIP;
 
     gu.out_f32 = Gb;
     if (ev0 && hipEventRecord(ev0, main) != hipSuccess) return ST_HIP;
-    if ((st = launch_gemm<MODE_GATEUP_F32>(gu, bm, main)) != ST_OK) return st;
+    if ((st = launch_gemm<MODE_GATEUP_F32>(gu, bm_gemm, main)) != ST_OK) return st;
     if (ev1 && hipEventRecord(ev1, main) != hipSuccess) return ST_HIP;
     if (lora_stream != main && hipStreamWaitEvent(main, sev->ready, 0) != hipSuccess) return ST_HIP;
     const long long nthr = (long long)R * (d.inter / 4);
