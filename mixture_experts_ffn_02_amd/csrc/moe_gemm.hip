@@ -692,6 +692,45 @@ void moe_gemm_kernel(const GemmParams P) {
       }
       return;
     }
+    if (BM <= 32 && BM * cpr * 2 <= NT) {
+      // all (row, 4-rank) pieces in one pass: each thread holds one f32x4 per split, so
+      // up to 16 splits load in one round trip in the registers that 8 splits of 8 ranks
+      // take (the decode down expand sums 12; on taller tiles the second code path put
+      // more registers in scratch)
+      constexpr int G4 = 16;
+      if (tid < BM * cpr * 2) {
+        const int r = tid / (2 * cpr), j0 = (tid % (2 * cpr)) * 4;
+        const int a = s_slot[r];
+        u32x2_t v2 = {0u, 0u};
+        if (a >= 0 && j0 < s_rank[a]) {
+          const f32x4_t *src = reinterpret_cast<const f32x4_t *>(P.part + (size_t)(row0 + r) * P.rmax + j0);
+          const size_t split_stride = (size_t)P.R * P.rmax / 4;  // in f32x4 units
+          float v[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int sp0 = 0; sp0 < P.part_splits; sp0 += G4) {
+            f32x4_t x[G4];
+#pragma unroll
+            for (int q = 0; q < G4; ++q) {
+              x[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              if (sp0 + q < P.part_splits) x[q] = src[(size_t)(sp0 + q) * split_stride];
+            }
+#pragma unroll
+            for (int q = 0; q < G4; ++q)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) v[t] += x[q][t];
+          }
+          const int ra_rank = s_rank[a];
+          const float sc = s_scal[a];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float lo = (j0 + 2 * q < ra_rank) ? v[2 * q] * sc : 0.f;
+            const float hi = (j0 + 2 * q + 1 < ra_rank) ? v[2 * q + 1] * sc : 0.f;
+            v2[q] = pack_bf16x2(lo, hi);
+          }
+        }
+        *reinterpret_cast<u32x2_t *>(&Xs[lds_off(r, j0 >> 3) + (j0 & 4)]) = v2;
+      }
+      return;
+    }
     for (int c = tid; c < BM * cpr; c += NT) {
       const int r = c / cpr, ch = c % cpr, j0 = ch * 8;
       const int a = s_slot[r];
