@@ -122,7 +122,8 @@ void moe_gemm_kernel(const GemmParams P) {
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int A_CH = BM * (BK / 8), B_CH = BN * (BK / 8);
-  // FP8 weights: 16-byte chunks of 16 codes (two bf16 LDS chunks each)
+  // FP8 weights: 16-byte chunks of 16 codes (two bf16 LDS chunks each, or one chunk of
+  // codes on the 16-row tiles)
   constexpr int B8_CH = BN * (BK / 16), B8_IT = (B8_CH + WM * WN * 64 - 1) / (WM * WN * 64);
   // slots whose expand B rows ride in the register stages at once (a deep FP8 pipeline
   // would otherwise multiply those registers)
@@ -440,7 +441,7 @@ void moe_gemm_kernel(const GemmParams P) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(bbase), (short)0, 0x7fffffff, 0x00020000);
     if constexpr (W8) {
       // FP8 weights (row-major, bbase = the expert's first code byte): 16 codes per chunk;
-      // store_lds scales them into bf16
+      // store_lds converts them into bf16 or, on 16-row tiles, stores the codes
       // (packed: the K step's blocks start k0 * N bytes into the expert's region)
       const int soff8 = decltype(pk)::value ? k0 * P.N : k0;
 #pragma unroll
@@ -490,7 +491,7 @@ void moe_gemm_kernel(const GemmParams P) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) *reinterpret_cast<u32x4_t *>(&As[buf][a_lds[i]]) = xa[i];
     if constexpr (W8) {
-      // 16 E4M3 codes (element j in byte j) -> bf16
+      // 16 E4M3 codes (element j in byte j): kept as codes, or -> bf16
       const int kb = step >> 1, KB = P.K / 128;
       if constexpr (kW8Raw) {
 #pragma unroll
@@ -672,8 +673,8 @@ void moe_gemm_kernel(const GemmParams P) {
   // the partials of up to G splits loaded together (one memory latency per group) and
   // summed in split order.
   auto build_xs = [&]() {
-    // splits loaded per round trip (decode: the gate_up shrink has 7 splits, the down
-    // expand 12; 4 at a time on 16-row tiles cost 1 % at decode against 8)
+    // splits loaded per round trip on the taller tiles (8 at a time against 4: 1 % at
+    // decode, measured when the 16-row tiles still took this path)
     constexpr int G = 8;
     const int cpr = P.rmax >> 3;  // 8-rank chunks that can hold data (rmax is a multiple of 8)
     // chunks past rmax are zero
