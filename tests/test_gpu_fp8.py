@@ -26,9 +26,17 @@ MID8 = make_config(name="fp8_mid_T512_H512_I256_E32_k8", cfg_id=212, T=512, H=51
                    slots=((32, 1.0), (16, 2.0), (8, 0.5)), slot_assignment="uniform")
 TALL8 = make_config(name="fp8_tall_T1024_H256_I256_E8_k2", cfg_id=213, T=1024, H=256, I=256, E=8, top_k=2,
                     slots=((16, 2.0),))
-# 16 rows per expert on average: 32-row gate_up tiles, 64-row down tiles
+# 16 rows per expert on average: 32-row gate_up and down tiles
 SHORT8 = make_config(name="fp8_short_T64_H512_I256_E32_k8", cfg_id=214, T=64, H=512, I=256, E=32, top_k=8,
                      slots=((16, 2.0), (32, 1.0)), slot_assignment="uniform")
+# 8 rows per expert on average: 16-row tiles, whose B stages keep the codes in LDS.  Tiles
+# with two slots, or one of rank above 32, stage the expand's B rows as bf16 through the
+# same buffers: loaded during the last K steps when the ranks are multiples of 8 (DEC8_MS),
+# after the K loop otherwise (DEC8_ODD)
+DEC8_MS = make_config(name="fp8_dec_T64_H512_I256_E64_k8_r16_64", cfg_id=217, T=64, H=512, I=256, E=64,
+                      top_k=8, slots=((16, 2.0), (64, 1.0)), slot_assignment="uniform")
+DEC8_ODD = make_config(name="fp8_dec_T64_H512_I256_E64_k8_r13_40", cfg_id=218, T=64, H=512, I=256, E=64,
+                       top_k=8, slots=((13, 2.0), (40, 0.5)), slot_assignment="uniform")
 
 
 def _stack(fn, E):
@@ -80,8 +88,10 @@ class Fp8Case:
 
 
 @pytest.mark.parametrize("cfg,with_lora", [(NAMED_CONFIGS[1], True), (NAMED_CONFIGS[2], True),
-                                           (NAMED_CONFIGS[2], False), (SHORT8, True), (MID8, True), (TALL8, True)],
-                         ids=["tiny", "decode", "decode-base", "short-32row", "mid-64row", "tall-128row"])
+                                           (NAMED_CONFIGS[2], False), (DEC8_MS, True), (DEC8_ODD, True),
+                                           (SHORT8, True), (MID8, True), (TALL8, True)],
+                         ids=["tiny", "decode", "decode-base", "16row-two-slots", "16row-odd-ranks",
+                              "short-32row", "mid-64row", "tall-128row"])
 def test_fp8_layer_parity(cfg, with_lora):
     say(f"[fp8] {cfg.name} lora={with_lora}")
     case = Fp8Case(cfg)
@@ -98,8 +108,8 @@ def _bf16_from_dequant(case, which):
     return t.to(dev())
 
 
-@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], MID8, TALL8],
-                         ids=["tiny", "decode", "mid-64row", "tall-128row"])
+@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], DEC8_MS, MID8, TALL8],
+                         ids=["tiny", "decode", "16row-two-slots", "mid-64row", "tall-128row"])
 def test_fp8_pow2_scales_bit_identical_to_bf16_kernels(cfg):
     say(f"[fp8 vs bf16] {cfg.name}")
     case = Fp8Case(cfg, pow2=True)
@@ -120,8 +130,9 @@ def test_fp8_pow2_scales_bit_identical_to_bf16_kernels(cfg):
     assert_layer_close(f64(out8), case.oracle()["out"], f"fp8 general path, pow2 scales {cfg.name}")
 
 
-@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], SHORT8, MID8, TALL8],
-                         ids=["tiny", "decode", "short-32row", "mid-64row", "tall-128row"])
+@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[1], NAMED_CONFIGS[2], DEC8_MS, DEC8_ODD, SHORT8, MID8, TALL8],
+                         ids=["tiny", "decode", "16row-two-slots", "16row-odd-ranks", "short-32row", "mid-64row",
+                              "tall-128row"])
 def test_fp8_packed_layouts_bit_identical(cfg):
     """The FP8 tile-packed layout (each weight alone and both) only reorders the codes."""
     say(f"[fp8 packed] {cfg.name}")
