@@ -142,6 +142,25 @@ def test_fp8_packed_layouts_bit_identical(cfg):
         assert torch.equal(case.run(packed=packed), ref), packed
 
 
+@pytest.mark.parametrize("cfg", [NAMED_CONFIGS[2], DEC8_MS], ids=["decode", "16row-two-slots"])
+def test_fp8_with_shared_outer_adapters(cfg):
+    """FP8 expert weights under the shared-outer LoRA layout (one gate_up A and one down B
+    per slot): held to the oracle, and bit-identical to the routed layout fed copies of the
+    shared matrices for every expert."""
+    say(f"[fp8 shared-outer] {cfg.name}")
+    case = Fp8Case(cfg)
+    c, g = case.cfg, case.g
+    layer = case.layer()
+    shared = layer(g.x, g.logits, g.lora_slots(shared_outer=True)).clone()
+    copies = layer(g.x, g.logits, g.lora_slots(replicate_shared=True)).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(shared, copies)
+    ref = oracle.layer(g.x_np, g.logits_np, c.top_k, c.I, case.w1, case.w2, g.oracle_adapters(shared_outer=True),
+                       g.slots_np, c.routing, g.bias_np, c.n_group, c.topk_group, c.routed_scaling_factor,
+                       num_experts=c.E)
+    assert_layer_close(f64(shared), ref["out"], f"fp8 shared-outer {cfg.name}")
+
+
 FINITE_E4M3 = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
 
 
