@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import GpuLayer, assert_layer_close, dev, f64, say
+from gpu_util import GpuLayer, assert_layer_close, dev, f64, say, t16
 from mixture_experts_ffn_02_amd import moe_lora as ml
 from synth import NAMED_CONFIGS, Workload, make_config
 
@@ -159,6 +159,54 @@ def test_fp8_with_shared_outer_adapters(cfg):
                        g.slots_np, c.routing, g.bias_np, c.n_group, c.topk_group, c.routed_scaling_factor,
                        num_experts=c.E)
     assert_layer_close(f64(shared), ref["out"], f"fp8 shared-outer {cfg.name}")
+
+
+def test_fp8_graph_replay_matches_oracle_and_eager():
+    """The FP8 layer's calls (route, forward, finalize) captured in a HIP graph at the decode
+    shape: every replay held to the oracle and equal to the eager result, with eager work
+    of the same layer between replays, and after new inputs are written into the captured
+    buffers."""
+    cfg = NAMED_CONFIGS[2]
+    say(f"[fp8 graph] {cfg.name}")
+    case = Fp8Case(cfg)
+    c, g = case.cfg, case.g
+    wl2 = Workload(cfg, 1)
+    x2_np, lg2_np = wl2.x(), wl2.logits()
+    x2, lg2 = t16(x2_np), t16(lg2_np)
+    want1 = case.oracle()["out"]
+    want2 = oracle.layer(x2_np, lg2_np, c.top_k, c.I, case.w1, case.w2, g.oracle_adapters(), g.slots_np,
+                         c.routing, g.bias_np, c.n_group, c.topk_group, c.routed_scaling_factor,
+                         num_experts=c.E)["out"]
+    layer, lora = case.layer(), g.lora_slots()
+    x_in, lg_in = g.x.clone(), g.logits.clone()  # the captured input buffers
+
+    def eager(x, lg):
+        out = layer(x, lg, lora).clone()
+        torch.cuda.synchronize()
+        return out
+
+    ref1 = eager(x_in, lg_in)  # also the warm-up
+    ref2 = eager(x2, lg2)
+    assert_layer_close(f64(ref1), want1, "fp8 eager, first inputs")
+    assert_layer_close(f64(ref2), want2, "fp8 eager, second inputs")
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = layer(x_in, lg_in, lora)
+    torch.cuda.synchronize()
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_layer_close(f64(out), want1, f"fp8 replay {i}")
+        assert torch.equal(out, ref1), f"fp8 replay {i} differs from the eager result"
+        assert torch.equal(eager(x2, lg2), ref2)
+    x_in.copy_(x2)
+    lg_in.copy_(lg2)
+    for i in range(2):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_layer_close(f64(out), want2, f"fp8 replay {i} on refilled inputs")
+        assert torch.equal(out, ref2), f"fp8 replay {i} on refilled inputs differs"
 
 
 FINITE_E4M3 = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
