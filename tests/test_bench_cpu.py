@@ -39,3 +39,16 @@ def test_committed_traffic_file_names_its_kernel_source():
     assert len(d["moe_gemm_sha"]) == 16
     recs = {k: v for k, v in d.items() if k != "moe_gemm_sha"}
     assert recs and all(v["traffic_bytes_per_launch"] > 0 for v in recs.values())
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """--gpus N > 1 exits (status 2) with a message before any GPU work: the layer runs on one
+    GPU's share of the experts."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
